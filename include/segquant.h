@@ -1,0 +1,217 @@
+/*
+ * segquant.h -- C ABI of libsegquant: the DualScale x SegLinear W8A8 linear
+ * layer on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [P1] "SegQuant: A Semantics-Aware and Generalizable Quantization
+ *        Framework for Diffusion Models", paper notes (papernotes.org,
+ *        CVPR 2026): "SegLinear" (output- and input-segmented patterns and
+ *        their equations), "DualScale" (split, scales, reconstruction,
+ *        hardware-native execution), framework table (AMax calibrator).
+ *   [P2] "SegQuant", project page (hliangzhao.me/works/segquant.html):
+ *        section 2 (SegLinear equations), section 3 (polarity-aware
+ *        quantisation Q_dual, s+ and s-, reconstruction, one batched launch
+ *        with a fused epilogue).
+ *
+ * What the layer computes (Y = X W, X in R^{M x K}, W in R^{K x N}):
+ *   split      X+ = max(X,0), X- = min(X,0)                     [P1 DualScale]
+ *   scales     s+ = max(X)/127, s- = |min(X)|/128, per K-segment  [P2 s.3]
+ *   quantise   q+ = clamp(rne(fp32(x+ * inv+)), 0, 127)
+ *              q- = clamp(rne(fp32(x- * inv-)), -128, 0)          [P2 s.3 Q_dual]
+ *   products   A+_i = q+_i W_q,i and A-_i = q-_i W_q,i (int32, exact) over
+ *              the K-range of segment i, both halves against one W tile
+ *   epilogue   y = sum_i w_scale[i][n] (s+_i A+_i + s-_i A-_i), fp32,
+ *              stored bf16 (round to nearest even)      [P1/P2 reconstruction]
+ * Output-segmented layers [P1 SegLinear pattern one] differ only in their
+ * weight-scale groups, which w_scale expresses per column; input-segmented
+ * layers [P1 SegLinear pattern two] carry one (s+, s-) pair and one weight
+ * scale group per K-segment.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates or frees device memory, keeps no pointer after the
+ *     call returns, and needs no workspace.
+ *   - Segment lists are HOST arrays (offset[n], width[n]), read only during
+ *     the call: offsets start at 0, are contiguous, widths are positive and
+ *     sum to the segmented dimension.  Every K-segment boundary except the
+ *     end of K is a multiple of 64 (one MFMA K-step); n <= SEGQ_MAX_KSEG.
+ *   - Activation scale table: DEVICE fp32 [4][n_kseg], rows
+ *     s_pos, s_neg, inv_pos, inv_neg (segquant_calibrate_amax writes it).
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major with a
+ *     leading dimension (elements) >= the row length.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; no call synchronises the host.
+ *   - Every call returns SEGQ_OK or a negative status.  All argument checks
+ *     run before any HIP call, so an invalid call enqueues nothing and
+ *     changes no buffer.  segquant_last_error() gives the thread's detail
+ *     text for its last failing call.  Nothing is thrown, printed or aborted.
+ *   - The library is thread-safe; its only state is that thread-local text.
+ *   - Inputs must not hold NaN.  +-Inf saturates to the end of its half's
+ *     code range when that half's inverse scale is nonzero; an infinite
+ *     value in a half whose scale is zero is outside the contract.
+ */
+#ifndef SEGQUANT_H
+#define SEGQUANT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SEGQ_OK 0
+#define SEGQ_ERR_NULL (-1)        /* a required pointer is NULL */
+#define SEGQ_ERR_SHAPE (-2)       /* a size or leading dimension is invalid */
+#define SEGQ_ERR_SEGMENTS (-3)    /* a segment list is malformed */
+#define SEGQ_ERR_ALIGN (-4)       /* a size, boundary or pointer is misaligned */
+#define SEGQ_ERR_UNSUPPORTED (-5) /* valid but beyond this library's limits */
+#define SEGQ_ERR_HIP (-6)         /* a HIP launch or runtime call failed */
+
+/* Limits. */
+#define SEGQ_MAX_KSEG 128
+/* Widest K-segment whose int32 products cannot overflow:
+ * floor((2^31 - 1) / (128 * 127)). */
+#define SEGQ_MAX_KSEG_WIDTH 132104
+
+/* Layouts of a quantised activation. */
+#define SEGQ_Q_SIGNED 0 /* one int8 plane [M][ld_q] holding q+ + q- (the
+                           halves have disjoint support, so this is lossless:
+                           q+ = max(Q,0), q- = min(Q,0)) */
+#define SEGQ_Q_PLANES 1 /* two int8 planes [2][M][ld_q]: q+ then q- */
+
+/* Flags for segquant_gemm_w8a8_seg. */
+#define SEGQ_GEMM_AUTO 0u        /* pick the kernel from the shape */
+#define SEGQ_GEMM_FORCE_TILE 1u  /* the MFMA tile kernel, any M */
+#define SEGQ_GEMM_FORCE_SMALLM 2u /* the weight-streaming kernel (M <= 16) */
+
+/* Kernel choices reported by segquant_gemm_kernel_for. */
+#define SEGQ_KERNEL_TILE 1
+#define SEGQ_KERNEL_SMALLM 2
+
+/*
+ * segquant_calibrate_amax -- AMax calibration of the static activation
+ * scales [P1 framework table, AMax; P1 DualScale scale equation; P2 s.3].
+ * For each K-segment i, over X[:, segment i]:
+ *   mx = max(0, max x), mn = min(0, min x)
+ *   s_pos = mx/127, s_neg = |mn|/128, inv_pos = 127/mx, inv_neg = 128/|mn|
+ * each quotient formed in fp64 and rounded once to fp32; an inverse whose
+ * range is zero is 0 (that half then quantises to all zeros).
+ *   x_bf16      device bf16 [M][ld_x]
+ *   act_scales  device fp32 [4][n_kseg] (output; also used as the reduction
+ *               buffer while the call runs)
+ * Three short launches on `stream`.  M may be 0 (all scales become 0).
+ */
+int segquant_calibrate_amax(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ld_x,
+                            int32_t n_kseg, const int32_t *kseg_offset,
+                            const int32_t *kseg_width, float *act_scales, void *stream);
+
+/*
+ * segquant_quantize_dualscale -- polarity split and dual-scale quantisation
+ * [P1 DualScale split and quantisation scheme; P2 s.3 Q_dual] of a bf16
+ * activation, HBM to HBM, for the pre-quantised GEMM path.
+ *   x_bf16      device bf16 [M][ld_x]
+ *   act_scales  device fp32 [4][n_kseg] (reads the inv rows)
+ *   q_out       device int8: SEGQ_Q_SIGNED -> [M][ld_q];
+ *               SEGQ_Q_PLANES -> [2][M][ld_q] (q+ plane, then q- plane)
+ * One launch.  M may be 0.
+ */
+int segquant_quantize_dualscale(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ld_x,
+                                int32_t n_kseg, const int32_t *kseg_offset,
+                                const int32_t *kseg_width, const float *act_scales,
+                                int8_t *q_out, int64_t ld_q, int32_t q_layout, void *stream);
+
+/*
+ * segquant_weight_packed_bytes -- size of the packed int8 weight for a
+ * K x N layer: K*N bytes when K % 64 == 0 and N % 16 == 0, else 0.
+ * The packed layout is tiles of 64 (k) x 16 (n) bytes, 1 KiB each, stored
+ * n-tile major: tile (nt, kt) at byte (nt * (K/64) + kt) * 1024; inside a
+ * tile, byte (g*16 + j)*16 + b holds W_q[kt*64 + g*16 + b][nt*16 + j]
+ * (g in 0..3, j in 0..15, b in 0..15): the operand order of the int8
+ * 16x16x64 matrix-core instruction, one 16-byte row per lane.
+ */
+size_t segquant_weight_packed_bytes(int64_t K, int64_t N);
+
+/*
+ * segquant_quantize_weight -- symmetric int8 weight quantisation per group
+ * [P1 SegLinear, both patterns: each segment quantised on its own; P2 s.2],
+ * packed for the kernels.  The group of (k, n) is (K-segment of k) x
+ * (N-segment of n), or (K-segment of k) x {n} when per_column != 0 (then
+ * the N-segment list is ignored and may be NULL).  Per group:
+ *   a = max |w|, s_w = a/127 and inv_w = 127/a (fp64 quotients rounded
+ *   once to fp32; inv_w = 0 when a = 0),
+ *   w_q = clamp(rne(fp32(w * inv_w)), -127, 127)
+ *   w          device fp32 [K][ld_w] (Y = X W)
+ *   w_packed   device int8, segquant_weight_packed_bytes(K, N) bytes
+ *   w_scale    device fp32 [n_kseg][N]: the s_w of the group holding
+ *              (K-segment i, column n) -- the epilogue's per-column scale
+ * Requires K % 64 == 0, N % 16 == 0.  Offline; four short launches.
+ */
+int segquant_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w,
+                             int32_t n_kseg, const int32_t *kseg_offset,
+                             const int32_t *kseg_width, int32_t n_nseg,
+                             const int32_t *nseg_offset, const int32_t *nseg_width,
+                             int32_t per_column, int8_t *w_packed, float *w_scale,
+                             void *stream);
+
+/*
+ * segquant_unpack_weight -- inverse of the packing: w_packed -> device int8
+ * W_q [K][ld_w] row-major.  For inspection and tests.  One launch.
+ */
+int segquant_unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t *w_kn,
+                           int64_t ld_w, void *stream);
+
+/*
+ * segquant_gemm_w8a8_seg -- the DualScale x SegLinear W8A8 linear layer in
+ * ONE launch [P1 DualScale hardware-native execution; P2 s.3: both polarity
+ * products in one batched launch, combined in a fused epilogue]:
+ *   y[m][n] = bf16( sum_i w_scale[i][n] * (s_pos[i]*A+_i[m][n]
+ *                                          + s_neg[i]*A-_i[m][n]) )
+ * with A+-_i the exact int32 products of the quantised halves over K-segment
+ * i against W_q (both halves read one W tile).  The activation is either
+ *   x_bf16 != NULL: bf16 [M][ld_x], quantised inside the kernel with the inv
+ *                   rows of act_scales (xq must be NULL), or
+ *   xq != NULL:     the output of segquant_quantize_dualscale with the same
+ *                   act_scales, layout q_layout, leading dimension ld_q.
+ *   w_packed   from segquant_quantize_weight (K x N)
+ *   w_scale    device fp32 [n_kseg][N]
+ *   act_scales device fp32 [4][n_kseg]
+ *   y_bf16     device bf16 [M][ld_y] (output)
+ *   acc_debug  optional device int32 [2][n_kseg][M][N]: when not NULL the
+ *              kernel also stores every per-segment accumulator A+_i
+ *              (plane 0) and A-_i (plane 1); NULL in production.
+ *   flags      SEGQ_GEMM_AUTO, or force one kernel for testing.
+ * Requires K % 64 == 0, N % 16 == 0, every K-segment width <=
+ * SEGQ_MAX_KSEG_WIDTH, 16-byte aligned tensor pointers, ld_x and ld_q
+ * multiples of 8 and 16 elements, ld_y a multiple of 2.  M may be 0 (no
+ * launch).  SEGQ_GEMM_FORCE_SMALLM requires M <= 16.
+ */
+int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
+                           const uint16_t *x_bf16, int64_t ld_x,
+                           const int8_t *xq, int64_t ld_q, int32_t q_layout,
+                           const int8_t *w_packed, const float *w_scale,
+                           int32_t n_kseg, const int32_t *kseg_offset,
+                           const int32_t *kseg_width, const float *act_scales,
+                           uint16_t *y_bf16, int64_t ld_y, int32_t *acc_debug,
+                           uint32_t flags, void *stream);
+
+/* Which kernel segquant_gemm_w8a8_seg runs for this shape under `flags`
+ * (SEGQ_KERNEL_*), or a negative status when the shape is invalid. */
+int segquant_gemm_kernel_for(int64_t M, int64_t N, int64_t K, uint32_t flags);
+
+/* Text for a status code (static storage). */
+const char *segquant_status_string(int status);
+
+/* Detail of this thread's last failing call ("" if none); valid until the
+ * thread's next call into the library. */
+const char *segquant_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int segquant_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEGQUANT_H */

@@ -95,14 +95,25 @@ void oracle_polarity_split(const uint16_t *x_bf16, int64_t n, float *x_pos, floa
   }
 }
 
+/* Scale and inverse of a range a >= 0 spread over `levels` steps:
+ * s = a/levels and inv = levels/a, each formed in fp64 and rounded once to
+ * fp32.  A zero range, or one so small that levels/a overflows fp32 (a below
+ * about 3.7e-37), counts as zero: s = inv = 0 (R5). */
+static void range_scale(double a, double levels, float *s, float *inv) {
+  float iv = a > 0.0 ? (float)(levels / a) : 0.0f;
+  if (isinf(iv)) iv = 0.0f;
+  *inv = iv;
+  *s = iv == 0.0f ? 0.0f : (float)(a / levels);
+}
+
 /* ------------------------------------------------------------------------
  * AMax activation calibration  [P1 framework table, AMax calibrator;
  * P1 "DualScale" scale equation; P2 section 3, s- and s+ definitions]
  * per K-segment i (R1, R5, R8):
  *   mx = max(0, max x),  mn = min(0, min x)   over X[:, segment i]
- *   s+ = mx / 127,   inv+ = 127 / mx  (0 when mx = 0)
- *   s- = |mn| / 128, inv- = 128 / |mn| (0 when mn = 0)
- * Each quotient is formed in fp64 and rounded once to fp32.
+ *   s+ = mx / 127,   inv+ = 127 / mx
+ *   s- = |mn| / 128, inv- = 128 / |mn|
+ * through range_scale (fp64 quotients rounded once; zero ranges give 0).
  * ---------------------------------------------------------------------- */
 int oracle_calibrate_amax(const uint16_t *x, int64_t M, int64_t K, int64_t ld,
                           int32_t n_kseg, const int32_t *koff, const int32_t *kwid,
@@ -116,18 +127,16 @@ int oracle_calibrate_amax(const uint16_t *x, int64_t M, int64_t K, int64_t ld,
         if (v > mx) mx = v;
         if (v < mn) mn = v;
       }
-    double amax_pos = (double)mx;
-    double amax_neg = -(double)mn;
-    s_pos[i] = (float)(amax_pos / 127.0);
-    s_neg[i] = (float)(amax_neg / 128.0);
-    inv_pos[i] = amax_pos > 0.0 ? (float)(127.0 / amax_pos) : 0.0f;
-    inv_neg[i] = amax_neg > 0.0 ? (float)(128.0 / amax_neg) : 0.0f;
+    range_scale((double)mx, 127.0, &s_pos[i], &inv_pos[i]);
+    range_scale(-(double)mn, 128.0, &s_neg[i], &inv_neg[i]);
   }
   return ORACLE_OK;
 }
 
-/* One half's code: rne of the fp32 product (R2, R3), then clamp (R4). */
+/* One half's code: rne of the fp32 product (R2, R3), then clamp (R4).
+ * A zero inverse means a zero range: that half is all zeros (R5). */
 static int32_t quant_code(float v_half, float inv, int32_t lo, int32_t hi) {
+  if (inv == 0.0f) return 0;
   float p = v_half * inv;          /* one IEEE binary32 multiply */
   float r = nearbyintf(p);         /* default mode: round half to even */
   if (r < (float)lo) return lo;    /* +-Inf saturate here */
@@ -167,7 +176,7 @@ int oracle_quantize_dualscale(const uint16_t *x, int64_t M, int64_t K, int64_t l
  * W is fp32 row-major [K][ldw] (Y = X W, W in R^{k x n}).  The group of
  * (k, n) is (K-segment of k) x (N-segment of n), or (K-segment of k) x
  * {column n} when per_column != 0.  Per group:
- *   a = max |w|;  s_w = a / 127;  inv_w = 127 / a (0 when a = 0)
+ *   a = max |w|;  s_w = a / 127;  inv_w = 127 / a   (range_scale)
  *   w_q = clamp(rne(w * inv_w), -127, 127)
  * Outputs: w_q int8 [K][N] and w_scale fp32 [n_kseg][N] (the s_w of the
  * group holding (segment i, column n)).
@@ -189,8 +198,8 @@ int oracle_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ldw,
           float v = fabsf(w[k * ldw + n]);
           if (v > a) a = v;
         }
-      float s_w = (float)((double)a / 127.0);
-      float inv_w = a > 0.0f ? (float)(127.0 / (double)a) : 0.0f;
+      float s_w, inv_w;
+      range_scale((double)a, 127.0, &s_w, &inv_w);
       for (int64_t n = n0; n < n1; ++n) w_scale[(int64_t)i * N + n] = s_w;
       for (int64_t k = koff[i]; k < (int64_t)koff[i] + kwid[i]; ++k)
         for (int64_t n = n0; n < n1; ++n)

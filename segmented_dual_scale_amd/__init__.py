@@ -1,3 +1,258 @@
-"""segmented_dual_scale_amd: the DualScale x SegLinear W8A8 linear layer on
-MI355X (gfx950).  The Python binding over the C-ABI library is added with
-the library itself; ``workloads`` holds the seeded input generators."""
+"""segmented_dual_scale_amd -- SegQuant's DualScale x SegLinear W8A8 linear
+layer on AMD Instinct MI355X (gfx950).
+
+This module is a thin ctypes binding over the C ABI of ``libsegquant.so``
+(``include/segquant.h``).  Each function has the name of its C entry point and
+only marshals arguments: torch supplies device memory and the current HIP
+stream, every step of the layer runs in the library's HIP kernels.  If the
+library is not built, every call raises: there is no other path.
+
+    from segmented_dual_scale_amd import (segquant_calibrate_amax,
+        segquant_quantize_weight, segquant_gemm_w8a8_seg)
+    act = segquant_calibrate_amax(x, kseg=[64] * 24)            # offline
+    wq, ws = segquant_quantize_weight(w, kseg=[64] * 24)        # offline
+    y = segquant_gemm_w8a8_seg(x, wq, ws, act, kseg=[64] * 24)  # one launch
+
+Pages: "SegQuant: A Semantics-Aware and Generalizable Quantization Framework
+for Diffusion Models" (papernotes.org notes, "SegLinear" and "DualScale"
+sections) and "SegQuant" (hliangzhao.me, sections 2 and 3).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+__all__ = [
+    "SegQuantError", "library_path", "load_library",
+    "segquant_calibrate_amax", "segquant_quantize_dualscale", "segquant_weight_packed_bytes",
+    "segquant_quantize_weight", "segquant_unpack_weight", "segquant_gemm_w8a8_seg",
+    "segquant_gemm_kernel_for", "segquant_status_string", "segquant_last_error",
+    "segquant_version", "SEGQ_Q_SIGNED", "SEGQ_Q_PLANES", "SEGQ_GEMM_AUTO",
+    "SEGQ_GEMM_FORCE_TILE", "SEGQ_GEMM_FORCE_SMALLM", "SEGQ_KERNEL_TILE", "SEGQ_KERNEL_SMALLM",
+]
+
+SEGQ_OK = 0
+SEGQ_ERR_NULL = -1
+SEGQ_ERR_SHAPE = -2
+SEGQ_ERR_SEGMENTS = -3
+SEGQ_ERR_ALIGN = -4
+SEGQ_ERR_UNSUPPORTED = -5
+SEGQ_ERR_HIP = -6
+SEGQ_MAX_KSEG = 128
+SEGQ_MAX_KSEG_WIDTH = 132104
+SEGQ_Q_SIGNED = 0
+SEGQ_Q_PLANES = 1
+SEGQ_GEMM_AUTO = 0
+SEGQ_GEMM_FORCE_TILE = 1
+SEGQ_GEMM_FORCE_SMALLM = 2
+SEGQ_KERNEL_TILE = 1
+SEGQ_KERNEL_SMALLM = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsegquant.so")
+_lib = None
+
+
+class SegQuantError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({segquant_status_string(status)}): {detail}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsegquant.so (built in-tree by segmented_dual_scale_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m segmented_dual_scale_amd.build` "
+                           "(the layer has no other implementation)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I32, U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+    sig = {
+        "segquant_calibrate_amax": [P, I64, I64, I64, I32, P, P, P, P],
+        "segquant_quantize_dualscale": [P, I64, I64, I64, I32, P, P, P, P, I64, I32, P],
+        "segquant_quantize_weight": [P, I64, I64, I64, I32, P, P, I32, P, P, I32, P, P, P],
+        "segquant_unpack_weight": [P, I64, I64, P, I64, P],
+        "segquant_gemm_w8a8_seg": [I64, I64, I64, P, I64, P, I64, I32, P, P, I32, P, P, P, P, I64,
+                                   P, U32, P],
+        "segquant_gemm_kernel_for": [I64, I64, I64, U32],
+        "segquant_version": [],
+        "segquant_status_string": [ctypes.c_int],
+        "segquant_last_error": [],
+        "segquant_weight_packed_bytes": [I64, I64],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.segquant_status_string.restype = ctypes.c_char_p
+    lib.segquant_last_error.restype = ctypes.c_char_p
+    lib.segquant_weight_packed_bytes.restype = ctypes.c_size_t
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------- helpers --
+def _segs(widths: Optional[Sequence[int]], total: int):
+    import numpy as np
+    w = np.asarray(list(widths) if widths is not None else [total], dtype=np.int32)
+    off = np.zeros_like(w)
+    if len(w) > 1:
+        off[1:] = np.cumsum(w)[:-1]
+    return off, w
+
+
+def _arr_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(rc: int, where: str):
+    if rc != SEGQ_OK:
+        raise SegQuantError(rc, where, segquant_last_error())
+
+
+def _ld(t, what: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{what} must be a 2-D tensor with unit stride in its last dimension")
+    return t.stride(0)
+
+
+# --------------------------------------------------------------- the ABI ----
+def segquant_status_string(status: int) -> str:
+    return load_library().segquant_status_string(status).decode()
+
+
+def segquant_last_error() -> str:
+    return load_library().segquant_last_error().decode()
+
+
+def segquant_version() -> int:
+    return load_library().segquant_version()
+
+
+def segquant_weight_packed_bytes(K: int, N: int) -> int:
+    return int(load_library().segquant_weight_packed_bytes(K, N))
+
+
+def segquant_gemm_kernel_for(M: int, N: int, K: int, flags: int = SEGQ_GEMM_AUTO) -> int:
+    return int(load_library().segquant_gemm_kernel_for(M, N, K, flags))
+
+
+def segquant_calibrate_amax(x, kseg: Optional[Sequence[int]] = None, out=None):
+    """AMax calibration: returns the fp32 [4][n_kseg] table (s+, s-, inv+,
+    inv-) for bf16 X [M][K] (device)."""
+    import torch
+    lib = load_library()
+    M, K = x.shape
+    off, wid = _segs(kseg, K)
+    if out is None:
+        out = torch.empty((4, len(wid)), dtype=torch.float32, device=x.device)
+    _check(lib.segquant_calibrate_amax(_ptr(x), M, K, _ld(x, "x"), len(wid), _arr_ptr(off),
+                                       _arr_ptr(wid), _ptr(out), _stream(x)),
+           "segquant_calibrate_amax")
+    return out
+
+
+def segquant_quantize_dualscale(x, act_scales, kseg: Optional[Sequence[int]] = None,
+                                layout: int = SEGQ_Q_SIGNED, out=None):
+    """Polarity split + dual-scale quantisation of bf16 X -> int8: [M][K]
+    signed codes, or [2][M][K] planes (q+, q-)."""
+    import torch
+    lib = load_library()
+    M, K = x.shape
+    off, wid = _segs(kseg, K)
+    if out is None:
+        ldq = (K + 15) // 16 * 16
+        shape = (M, ldq) if layout == SEGQ_Q_SIGNED else (2, M, ldq)
+        out = torch.empty(shape, dtype=torch.int8, device=x.device)
+    ld_q = out.stride(-2)
+    _check(lib.segquant_quantize_dualscale(_ptr(x), M, K, _ld(x, "x"), len(wid), _arr_ptr(off),
+                                           _arr_ptr(wid), _ptr(act_scales), _ptr(out), ld_q,
+                                           layout, _stream(x)),
+           "segquant_quantize_dualscale")
+    return out
+
+
+def segquant_quantize_weight(w, kseg: Optional[Sequence[int]] = None,
+                             nseg: Optional[Sequence[int]] = None, per_column: bool = False,
+                             out_packed=None, out_scale=None) -> Tuple:
+    """Per-group symmetric int8 quantisation of fp32 W [K][N] (device):
+    returns (packed int8 weight, fp32 w_scale [n_kseg][N])."""
+    import torch
+    lib = load_library()
+    K, N = w.shape
+    koff, kwid = _segs(kseg, K)
+    noff, nwid = _segs(nseg, N)
+    if out_packed is None:
+        nbytes = segquant_weight_packed_bytes(K, N)
+        out_packed = torch.empty(max(nbytes, 16), dtype=torch.int8, device=w.device)
+    if out_scale is None:
+        out_scale = torch.empty((len(kwid), N), dtype=torch.float32, device=w.device)
+    _check(lib.segquant_quantize_weight(_ptr(w), K, N, _ld(w, "w"), len(kwid), _arr_ptr(koff),
+                                        _arr_ptr(kwid), len(nwid), _arr_ptr(noff), _arr_ptr(nwid),
+                                        int(bool(per_column)), _ptr(out_packed), _ptr(out_scale),
+                                        _stream(w)),
+           "segquant_quantize_weight")
+    return out_packed, out_scale
+
+
+def segquant_unpack_weight(w_packed, K: int, N: int, out=None):
+    """Packed weight -> int8 W_q [K][N] (for inspection)."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty((K, N), dtype=torch.int8, device=w_packed.device)
+    _check(lib.segquant_unpack_weight(_ptr(w_packed), K, N, _ptr(out), _ld(out, "out"),
+                                      _stream(w_packed)),
+           "segquant_unpack_weight")
+    return out
+
+
+def segquant_gemm_w8a8_seg(x, w_packed, w_scale, act_scales, kseg: Optional[Sequence[int]] = None,
+                           N: Optional[int] = None, xq=None, q_layout: int = SEGQ_Q_SIGNED,
+                           out=None, acc_debug=None, flags: int = SEGQ_GEMM_AUTO):
+    """The DualScale x SegLinear W8A8 layer in one launch.
+
+    x: bf16 [M][K] (or None with xq = the output of
+    segquant_quantize_dualscale); w_packed/w_scale from
+    segquant_quantize_weight; act_scales from segquant_calibrate_amax.
+    Returns bf16 Y [M][N].  acc_debug, if given, is an int32 tensor
+    [2][n_kseg][M][N] that receives the per-segment accumulators."""
+    import torch
+    lib = load_library()
+    src = x if x is not None else xq
+    if x is not None:
+        M, K = x.shape
+        ld_x, ld_q = _ld(x, "x"), 0
+    else:
+        M = xq.shape[-2]
+        K = sum(kseg) if kseg is not None else None
+        if K is None:
+            raise ValueError("kseg is required with a pre-quantised input")
+        ld_x, ld_q = 0, xq.stride(-2)
+    if N is None:
+        N = w_scale.shape[1]
+    off, wid = _segs(kseg, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=src.device)
+    _check(lib.segquant_gemm_w8a8_seg(M, N, K, _ptr(x), ld_x, _ptr(xq), ld_q, q_layout,
+                                      _ptr(w_packed), _ptr(w_scale), len(wid), _arr_ptr(off),
+                                      _arr_ptr(wid), _ptr(act_scales), _ptr(out), _ld(out, "out"),
+                                      _ptr(acc_debug), flags, _stream(src)),
+           "segquant_gemm_w8a8_seg")
+    return out

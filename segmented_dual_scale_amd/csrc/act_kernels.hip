@@ -1,0 +1,191 @@
+// act_kernels.hip -- activation-side kernels for gfx950:
+//   * AMax calibration of the static DualScale scales
+//     [P1 framework table, AMax calibrator; P1 "DualScale" scale equation;
+//      P2 section 3, s+ = max/127 and s- = |min|/128], and
+//   * the standalone polarity split + dual-scale quantisation
+//     [P1 "DualScale" split and quantisation; P2 section 3, Q_dual], an
+//     HBM-streaming kernel: 2 bytes read and 1 (signed code) or 2 (two
+//     planes) bytes written per element.
+//
+// [P1] "SegQuant: A Semantics-Aware and Generalizable Quantization Framework
+//      for Diffusion Models" (papernotes.org notes).
+// [P2] "SegQuant" (hliangzhao.me).
+//
+// Work split: a 2-D grid, blockIdx.y = K-segment (so its scales are uniform
+// across the workgroup and live in scalar registers), blockIdx.x = a block
+// of rows.  Inside a workgroup each wave walks rows; L lanes (a power of two
+// up to 64) share one row and step through it 8 elements (16 bytes) at a
+// time, so narrow segments (64 columns = 8 chunks) still fill the wave.
+#include "sq_device.hpp"
+#include "sq_launch.hpp"
+
+namespace sq {
+
+namespace {
+
+struct ActArgs {
+  const uint16_t *x;
+  int64_t M, K, ld_x;
+  int32_t rows_per_block;
+  int32_t lanes_log2;  // lanes sharing one row
+  const float *act;    // [4][n_kseg]
+  float *act_out;      // the same table, written by calibration
+  int8_t *q;
+  int64_t ld_q;
+  int64_t plane_stride;  // elements between the + and - planes (0: signed)
+  int32_t n_kseg;
+  SegTable ks;
+};
+
+__device__ __forceinline__ v4u load_x8(const uint16_t *p) {
+  return *reinterpret_cast<const v4u *>(p);
+}
+
+// Tail of a row whose length is not a multiple of 8: element by element.
+__device__ __forceinline__ uint32_t load_bf16(const uint16_t *p) { return *p; }
+
+__global__ void calib_init_kernel(float *act, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < 2 * n) act[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void calib_reduce_kernel(ActArgs a) {
+  const int seg = blockIdx.y;
+  const int64_t k0 = a.ks.off[seg], k1 = a.ks.end[seg];
+  const int L = 1 << a.lanes_log2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane >> a.lanes_log2, col = lane & (L - 1);
+  const int rows_per_step = (64 >> a.lanes_log2) * (blockDim.x >> 6);
+  const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
+  const int64_t r1 = min(r0 + a.rows_per_block, a.M);
+  float mp = 0.0f, mn = 0.0f;
+  for (int64_t r = r0 + wave * (64 >> a.lanes_log2) + sub; r < r1; r += rows_per_step) {
+    const uint16_t *row = a.x + r * a.ld_x;
+    int64_t k = k0 + 8 * col;
+    for (; k + 8 <= k1; k += 8 * L) {
+      v4u v = load_x8(row + k);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float lo = bf16_lo(v[j]), hi = bf16_hi(v[j]);
+        mp = fmaxf(mp, fmaxf(pos_part(lo), pos_part(hi)));
+        mn = fmaxf(mn, fmaxf(neg_mag(lo), neg_mag(hi)));
+      }
+    }
+    for (int64_t kk = k; kk < k1 && kk < k + 8; ++kk) {
+      float f = __uint_as_float(load_bf16(row + kk) << 16);
+      mp = fmaxf(mp, pos_part(f));
+      mn = fmaxf(mn, neg_mag(f));
+    }
+  }
+  mp = wave_max(mp);
+  mn = wave_max(mn);
+  if (lane == 0) {
+    atomicMax(reinterpret_cast<unsigned *>(a.act_out) + seg, __float_as_uint(mp));
+    atomicMax(reinterpret_cast<unsigned *>(a.act_out) + a.n_kseg + seg, __float_as_uint(mn));
+  }
+}
+
+__global__ void calib_finalize_kernel(float *act, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float mx = act[i], mn = act[n + i];
+  float sp, ip, sn, in;
+  scale_pair(mx, 127.0, sp, ip);
+  scale_pair(mn, 128.0, sn, in);
+  act[i] = sp;
+  act[n + i] = sn;
+  act[2 * n + i] = ip;
+  act[3 * n + i] = in;
+}
+
+template <bool PLANES>
+__global__ __launch_bounds__(256) void quantize_kernel(ActArgs a) {
+  const int seg = blockIdx.y;
+  const int64_t k0 = a.ks.off[seg], k1 = a.ks.end[seg];
+  const float inv_pos = a.act[2 * a.n_kseg + seg];
+  const float inv_neg = a.act[3 * a.n_kseg + seg];
+  const int L = 1 << a.lanes_log2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane >> a.lanes_log2, col = lane & (L - 1);
+  const int rows_per_step = (64 >> a.lanes_log2) * (blockDim.x >> 6);
+  const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
+  const int64_t r1 = min(r0 + a.rows_per_block, a.M);
+  for (int64_t r = r0 + wave * (64 >> a.lanes_log2) + sub; r < r1; r += rows_per_step) {
+    const uint16_t *row = a.x + r * a.ld_x;
+    int8_t *qrow = a.q + r * a.ld_q;
+    int64_t k = k0 + 8 * col;
+    for (; k + 8 <= k1; k += 8 * L) {
+      v4u v = load_x8(row + k);
+      if (PLANES) {
+        v2u p, n;
+        quant8_planes(v, inv_pos, inv_neg, p, n);
+        *reinterpret_cast<v2u *>(qrow + k) = p;
+        *reinterpret_cast<v2u *>(qrow + a.plane_stride + k) = n;
+      } else {
+        *reinterpret_cast<v2u *>(qrow + k) = quant8_signed(v, inv_pos, inv_neg);
+      }
+    }
+    for (int64_t kk = k; kk < k1 && kk < k + 8; ++kk) {
+      float f = __uint_as_float(load_bf16(row + kk) << 16);
+      int8_t code = (int8_t)(quant_magic(f, inv_pos, inv_neg) & 0xffu);
+      if (PLANES) {
+        qrow[kk] = code > 0 ? code : 0;
+        qrow[a.plane_stride + kk] = code < 0 ? code : 0;
+      } else {
+        qrow[kk] = code;
+      }
+    }
+  }
+}
+
+// Rows per workgroup and lanes per row for a segment layout: aim for about
+// 16K elements per workgroup on the widest segment.
+void plan_rows(int64_t M, const SegTable &ks, ActArgs &a) {
+  int64_t wmax = 0;
+  for (int i = 0; i < ks.n; ++i) wmax = wmax > ks.end[i] - ks.off[i] ? wmax : ks.end[i] - ks.off[i];
+  int64_t chunks = (wmax + 7) / 8;
+  int lg = 0;
+  while ((1 << lg) < chunks && lg < 6) ++lg;
+  a.lanes_log2 = lg;
+  int64_t rows_per_step = (64 >> lg) * 4;
+  int64_t rows = (16384 + wmax - 1) / wmax;
+  rows = ((rows + rows_per_step - 1) / rows_per_step) * rows_per_step;
+  if (rows > M) rows = M < 1 ? 1 : M;
+  a.rows_per_block = (int32_t)rows;
+}
+
+}  // namespace
+
+hipError_t launch_calibrate(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
+                            const SegTable &ks, float *act, hipStream_t s) {
+  const int n = ks.n;
+  hipLaunchKernelGGL(calib_init_kernel, dim3((2 * n + 255) / 256), dim3(256), 0, s, act, n);
+  if (M > 0) {
+    ActArgs a{};
+    a.x = x; a.M = M; a.K = K; a.ld_x = ld_x; a.act = act; a.act_out = act; a.n_kseg = n; a.ks = ks;
+    plan_rows(M, ks, a);
+    dim3 grid((unsigned)((M + a.rows_per_block - 1) / a.rows_per_block), (unsigned)n);
+    hipLaunchKernelGGL(calib_reduce_kernel, grid, dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL(calib_finalize_kernel, dim3((n + 255) / 256), dim3(256), 0, s, act, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
+                           const SegTable &ks, const float *act, int8_t *q, int64_t ld_q,
+                           int32_t layout, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  ActArgs a{};
+  a.x = x; a.M = M; a.K = K; a.ld_x = ld_x; a.act = act; a.q = q; a.ld_q = ld_q;
+  a.n_kseg = ks.n; a.ks = ks;
+  a.plane_stride = layout ? M * ld_q : 0;
+  plan_rows(M, ks, a);
+  dim3 grid((unsigned)((M + a.rows_per_block - 1) / a.rows_per_block), (unsigned)ks.n);
+  if (layout)
+    hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace sq

@@ -1,0 +1,278 @@
+// api.cpp -- the C ABI of libsegquant (declared in include/segquant.h):
+// argument validation, segment tables, kernel choice and launch.
+//
+// Every check runs before the first HIP call, so an invalid call enqueues
+// nothing, touches no buffer and behaves the same on a machine without a
+// GPU.  Errors are returned as status codes with a thread-local detail text;
+// nothing is thrown across the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/segquant.h"
+#include "sq_launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int ok() {
+  g_err.clear();
+  return SEGQ_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kI32Max = 0x7fffffff;
+
+// K-segment list -> kernel table.  require64: every boundary but the end of
+// K is a multiple of 64; max_width: 0 for no limit.
+int read_kseg(int32_t n, const int32_t *off, const int32_t *wid, int64_t K, int64_t max_width,
+              sq::SegTable &t) {
+  if (n < 1) return fail(SEGQ_ERR_SEGMENTS, "K-segment count %d < 1", n);
+  if (n > SEGQ_MAX_KSEG)
+    return fail(SEGQ_ERR_UNSUPPORTED, "K-segment count %d > %d", n, SEGQ_MAX_KSEG);
+  if (!off || !wid) return fail(SEGQ_ERR_NULL, "K-segment offset/width array is NULL");
+  int64_t at = 0;
+  t.n = n;
+  for (int32_t i = 0; i < n; ++i) {
+    if (off[i] != at)
+      return fail(SEGQ_ERR_SEGMENTS, "K-segment %d starts at %d, expected %lld", i, off[i],
+                  (long long)at);
+    if (wid[i] <= 0) return fail(SEGQ_ERR_SEGMENTS, "K-segment %d has width %d", i, wid[i]);
+    if (max_width > 0 && wid[i] > max_width)
+      return fail(SEGQ_ERR_UNSUPPORTED, "K-segment %d width %d exceeds %lld (int32 bound)", i,
+                  wid[i], (long long)max_width);
+    at += wid[i];
+    if (at < K && at % 64 != 0)
+      return fail(SEGQ_ERR_ALIGN, "K-segment boundary %lld is not a multiple of 64",
+                  (long long)at);
+    t.off[i] = off[i];
+    t.end[i] = (int32_t)at;
+  }
+  if (at != K)
+    return fail(SEGQ_ERR_SEGMENTS, "K-segments cover %lld columns, K is %lld", (long long)at,
+                (long long)K);
+  return SEGQ_OK;
+}
+
+int read_nseg(int32_t n, const int32_t *off, const int32_t *wid, int64_t N, sq::NSegTable &t) {
+  if (n < 1) return fail(SEGQ_ERR_SEGMENTS, "N-segment count %d < 1", n);
+  if (n > sq::kMaxNSeg) return fail(SEGQ_ERR_UNSUPPORTED, "N-segment count %d > %d", n, sq::kMaxNSeg);
+  if (!off || !wid) return fail(SEGQ_ERR_NULL, "N-segment offset/width array is NULL");
+  int64_t at = 0;
+  t.n = n;
+  for (int32_t i = 0; i < n; ++i) {
+    if (off[i] != at)
+      return fail(SEGQ_ERR_SEGMENTS, "N-segment %d starts at %d, expected %lld", i, off[i],
+                  (long long)at);
+    if (wid[i] <= 0) return fail(SEGQ_ERR_SEGMENTS, "N-segment %d has width %d", i, wid[i]);
+    at += wid[i];
+    t.off[i] = off[i];
+    t.end[i] = (int32_t)at;
+  }
+  if (at != N)
+    return fail(SEGQ_ERR_SEGMENTS, "N-segments cover %lld columns, N is %lld", (long long)at,
+                (long long)N);
+  return SEGQ_OK;
+}
+
+int check_x(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x) {
+  if (M < 0 || K < 1 || M > kI32Max || K > kI32Max)
+    return fail(SEGQ_ERR_SHAPE, "bad shape M=%lld K=%lld", (long long)M, (long long)K);
+  if (ld_x < K) return fail(SEGQ_ERR_SHAPE, "ld_x %lld < K %lld", (long long)ld_x, (long long)K);
+  if (M > 0 && !x) return fail(SEGQ_ERR_NULL, "x_bf16 is NULL");
+  if (ld_x % 8 != 0) return fail(SEGQ_ERR_ALIGN, "ld_x %lld is not a multiple of 8", (long long)ld_x);
+  if (x && !aligned16(x)) return fail(SEGQ_ERR_ALIGN, "x_bf16 is not 16-byte aligned");
+  return SEGQ_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(SEGQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *segquant_status_string(int status) {
+  switch (status) {
+    case SEGQ_OK: return "ok";
+    case SEGQ_ERR_NULL: return "null pointer";
+    case SEGQ_ERR_SHAPE: return "invalid shape";
+    case SEGQ_ERR_SEGMENTS: return "invalid segment list";
+    case SEGQ_ERR_ALIGN: return "misaligned size, boundary or pointer";
+    case SEGQ_ERR_UNSUPPORTED: return "unsupported (beyond library limits)";
+    case SEGQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *segquant_last_error(void) { return g_err.c_str(); }
+
+int segquant_version(void) { return 100; }
+
+size_t segquant_weight_packed_bytes(int64_t K, int64_t N) {
+  if (K < 64 || N < 16 || K % 64 || N % 16 || K > kI32Max || N > kI32Max) return 0;
+  return (size_t)K * (size_t)N;
+}
+
+int segquant_calibrate_amax(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ld_x,
+                            int32_t n_kseg, const int32_t *kseg_offset,
+                            const int32_t *kseg_width, float *act_scales, void *stream) {
+  int st = check_x(x_bf16, M, K, ld_x);
+  if (st) return st;
+  if (!act_scales) return fail(SEGQ_ERR_NULL, "act_scales is NULL");
+  sq::SegTable ks{};
+  if ((st = read_kseg(n_kseg, kseg_offset, kseg_width, K, 0, ks))) return st;
+  return hip_status(sq::launch_calibrate(x_bf16, M, K, ld_x, ks, act_scales, (hipStream_t)stream),
+                    "calibrate launch");
+}
+
+int segquant_quantize_dualscale(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ld_x,
+                                int32_t n_kseg, const int32_t *kseg_offset,
+                                const int32_t *kseg_width, const float *act_scales,
+                                int8_t *q_out, int64_t ld_q, int32_t q_layout, void *stream) {
+  int st = check_x(x_bf16, M, K, ld_x);
+  if (st) return st;
+  if (!act_scales) return fail(SEGQ_ERR_NULL, "act_scales is NULL");
+  if (M > 0 && !q_out) return fail(SEGQ_ERR_NULL, "q_out is NULL");
+  if (q_layout != SEGQ_Q_SIGNED && q_layout != SEGQ_Q_PLANES)
+    return fail(SEGQ_ERR_SHAPE, "unknown q_layout %d", q_layout);
+  if (ld_q < K) return fail(SEGQ_ERR_SHAPE, "ld_q %lld < K %lld", (long long)ld_q, (long long)K);
+  if (ld_q % 16 != 0) return fail(SEGQ_ERR_ALIGN, "ld_q %lld is not a multiple of 16", (long long)ld_q);
+  if (q_out && !aligned16(q_out)) return fail(SEGQ_ERR_ALIGN, "q_out is not 16-byte aligned");
+  sq::SegTable ks{};
+  if ((st = read_kseg(n_kseg, kseg_offset, kseg_width, K, 0, ks))) return st;
+  return hip_status(sq::launch_quantize(x_bf16, M, K, ld_x, ks, act_scales, q_out, ld_q, q_layout,
+                                        (hipStream_t)stream),
+                    "quantize launch");
+}
+
+int segquant_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w,
+                             int32_t n_kseg, const int32_t *kseg_offset,
+                             const int32_t *kseg_width, int32_t n_nseg,
+                             const int32_t *nseg_offset, const int32_t *nseg_width,
+                             int32_t per_column, int8_t *w_packed, float *w_scale,
+                             void *stream) {
+  if (K < 1 || N < 1 || K > kI32Max || N > kI32Max)
+    return fail(SEGQ_ERR_SHAPE, "bad shape K=%lld N=%lld", (long long)K, (long long)N);
+  if (ld_w < N) return fail(SEGQ_ERR_SHAPE, "ld_w %lld < N %lld", (long long)ld_w, (long long)N);
+  if (!w || !w_packed || !w_scale) return fail(SEGQ_ERR_NULL, "w, w_packed or w_scale is NULL");
+  if (K % 64 || N % 16)
+    return fail(SEGQ_ERR_ALIGN, "weight needs K %% 64 == 0 and N %% 16 == 0 (K=%lld N=%lld)",
+                (long long)K, (long long)N);
+  if (!aligned16(w_packed) || (reinterpret_cast<uintptr_t>(w) & 3u))
+    return fail(SEGQ_ERR_ALIGN, "w_packed must be 16-byte and w 4-byte aligned");
+  sq::SegTable ks{};
+  int st = read_kseg(n_kseg, kseg_offset, kseg_width, K, 0, ks);
+  if (st) return st;
+  sq::NSegTable ns{};
+  ns.n = 1;
+  ns.off[0] = 0;
+  ns.end[0] = (int32_t)N;
+  if (!per_column && (st = read_nseg(n_nseg, nseg_offset, nseg_width, N, ns))) return st;
+  return hip_status(sq::launch_quantize_weight(w, K, N, ld_w, ks, ns, per_column != 0, w_packed,
+                                               w_scale, (hipStream_t)stream),
+                    "quantize_weight launch");
+}
+
+int segquant_unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t *w_kn,
+                           int64_t ld_w, void *stream) {
+  if (segquant_weight_packed_bytes(K, N) == 0)
+    return fail(SEGQ_ERR_ALIGN, "weight needs K %% 64 == 0 and N %% 16 == 0 (K=%lld N=%lld)",
+                (long long)K, (long long)N);
+  if (ld_w < N) return fail(SEGQ_ERR_SHAPE, "ld_w %lld < N %lld", (long long)ld_w, (long long)N);
+  if (!w_packed || !w_kn) return fail(SEGQ_ERR_NULL, "w_packed or w_kn is NULL");
+  if (!aligned16(w_packed)) return fail(SEGQ_ERR_ALIGN, "w_packed is not 16-byte aligned");
+  return hip_status(sq::launch_unpack_weight(w_packed, K, N, w_kn, ld_w, (hipStream_t)stream),
+                    "unpack launch");
+}
+
+static int gemm_check(int64_t M, int64_t N, int64_t K, uint32_t flags) {
+  if (M < 0 || N < 1 || K < 1 || M > kI32Max || N > kI32Max || K > kI32Max)
+    return fail(SEGQ_ERR_SHAPE, "bad shape M=%lld N=%lld K=%lld", (long long)M, (long long)N,
+                (long long)K);
+  if (K % 64 || N % 16)
+    return fail(SEGQ_ERR_ALIGN, "GEMM needs K %% 64 == 0 and N %% 16 == 0 (K=%lld N=%lld)",
+                (long long)K, (long long)N);
+  if (flags & ~(SEGQ_GEMM_FORCE_TILE | SEGQ_GEMM_FORCE_SMALLM))
+    return fail(SEGQ_ERR_SHAPE, "unknown flags 0x%x", flags);
+  if ((flags & SEGQ_GEMM_FORCE_TILE) && (flags & SEGQ_GEMM_FORCE_SMALLM))
+    return fail(SEGQ_ERR_SHAPE, "both kernels forced");
+  if ((flags & SEGQ_GEMM_FORCE_SMALLM) && M > sq::kSmallMMax)
+    return fail(SEGQ_ERR_UNSUPPORTED, "the small-M kernel takes M <= %d (M=%lld)", sq::kSmallMMax,
+                (long long)M);
+  return SEGQ_OK;
+}
+
+int segquant_gemm_kernel_for(int64_t M, int64_t N, int64_t K, uint32_t flags) {
+  int st = gemm_check(M, N, K, flags);
+  if (st) return st;
+  if (flags & SEGQ_GEMM_FORCE_TILE) return SEGQ_KERNEL_TILE;
+  if (flags & SEGQ_GEMM_FORCE_SMALLM) return SEGQ_KERNEL_SMALLM;
+  return M <= sq::kSmallMMax ? SEGQ_KERNEL_SMALLM : SEGQ_KERNEL_TILE;
+}
+
+int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
+                           const uint16_t *x_bf16, int64_t ld_x,
+                           const int8_t *xq, int64_t ld_q, int32_t q_layout,
+                           const int8_t *w_packed, const float *w_scale,
+                           int32_t n_kseg, const int32_t *kseg_offset,
+                           const int32_t *kseg_width, const float *act_scales,
+                           uint16_t *y_bf16, int64_t ld_y, int32_t *acc_debug,
+                           uint32_t flags, void *stream) {
+  int st = gemm_check(M, N, K, flags);
+  if (st) return st;
+  if (M > 0) {
+    if ((x_bf16 != nullptr) == (xq != nullptr))
+      return fail(SEGQ_ERR_NULL, "exactly one of x_bf16 and xq must be given");
+    if (x_bf16) {
+      if ((st = check_x(x_bf16, M, K, ld_x))) return st;
+    } else {
+      if (q_layout != SEGQ_Q_SIGNED && q_layout != SEGQ_Q_PLANES)
+        return fail(SEGQ_ERR_SHAPE, "unknown q_layout %d", q_layout);
+      if (ld_q < K) return fail(SEGQ_ERR_SHAPE, "ld_q %lld < K %lld", (long long)ld_q, (long long)K);
+      if (ld_q % 16 != 0)
+        return fail(SEGQ_ERR_ALIGN, "ld_q %lld is not a multiple of 16", (long long)ld_q);
+      if (!aligned16(xq)) return fail(SEGQ_ERR_ALIGN, "xq is not 16-byte aligned");
+    }
+    if (!w_packed || !w_scale || !act_scales || !y_bf16)
+      return fail(SEGQ_ERR_NULL, "w_packed, w_scale, act_scales or y_bf16 is NULL");
+    if (!aligned16(w_packed)) return fail(SEGQ_ERR_ALIGN, "w_packed is not 16-byte aligned");
+    if (ld_y < N) return fail(SEGQ_ERR_SHAPE, "ld_y %lld < N %lld", (long long)ld_y, (long long)N);
+    if ((reinterpret_cast<uintptr_t>(y_bf16) & 1u) ||
+        (acc_debug && (reinterpret_cast<uintptr_t>(acc_debug) & 3u)))
+      return fail(SEGQ_ERR_ALIGN, "y_bf16 or acc_debug is misaligned");
+  }
+  sq::SegTable ks{};
+  if ((st = read_kseg(n_kseg, kseg_offset, kseg_width, K, SEGQ_MAX_KSEG_WIDTH, ks))) return st;
+  if (M == 0) return ok();
+  sq::GemmProblem p{};
+  p.M = M; p.N = N; p.K = K;
+  p.x = x_bf16; p.ld_x = ld_x;
+  p.xq = xq; p.ld_q = ld_q; p.q_layout = q_layout;
+  p.w_packed = w_packed; p.w_scale = w_scale; p.act = act_scales;
+  p.ks = ks;
+  p.y = y_bf16; p.ld_y = ld_y; p.acc_debug = acc_debug;
+  const int kernel = segquant_gemm_kernel_for(M, N, K, flags);
+  hipError_t e = kernel == SEGQ_KERNEL_SMALLM ? sq::launch_gemm_smallm(p, (hipStream_t)stream)
+                                              : sq::launch_gemm_tile(p, (hipStream_t)stream);
+  return hip_status(e, "gemm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// sq_launch.hpp -- host-side launch interface between the C-ABI front end
+// (api.cpp) and the kernels.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sq {
+
+constexpr int kMaxKSeg = 128;
+constexpr int kMaxNSeg = 128;
+
+// A segmented dimension in the form the kernels read from their arguments.
+struct SegTable {
+  int32_t n;
+  int32_t off[kMaxKSeg];
+  int32_t end[kMaxKSeg];  // exclusive
+};
+
+struct NSegTable {
+  int32_t n;
+  int32_t off[kMaxNSeg];
+  int32_t end[kMaxNSeg];
+};
+
+hipError_t launch_calibrate(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
+                            const SegTable &ks, float *act, hipStream_t s);
+
+hipError_t launch_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
+                           const SegTable &ks, const float *act, int8_t *q, int64_t ld_q,
+                           int32_t layout, hipStream_t s);
+
+hipError_t launch_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w,
+                                  const SegTable &ks, const NSegTable &ns, bool per_column,
+                                  int8_t *w_packed, float *w_scale, hipStream_t s);
+
+hipError_t launch_unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t *w_kn,
+                                int64_t ld_w, hipStream_t s);
+
+struct GemmProblem {
+  int64_t M, N, K;
+  const uint16_t *x;
+  int64_t ld_x;
+  const int8_t *xq;
+  int64_t ld_q;
+  int32_t q_layout;
+  const int8_t *w_packed;
+  const float *w_scale;
+  const float *act;
+  SegTable ks;
+  uint16_t *y;
+  int64_t ld_y;
+  int32_t *acc_debug;
+};
+
+hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s);
+hipError_t launch_gemm_smallm(const GemmProblem &p, hipStream_t s);
+
+constexpr int kSmallMMax = 16;
+
+}  // namespace sq

@@ -1,0 +1,207 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: activation scales, int8 codes (both layouts), packed weights and
+weight scales, and every per-segment int32 accumulator.  Within
+|y - y_ref| <= 8e-3 |y_ref| + 1e-3 max|y_ref|: the bf16 output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import segmented_dual_scale_amd as S
+from segmented_dual_scale_amd import workloads as W
+from gpu_common import (DEV, GpuLayer, OracleLayer, bf16_dev_to_f64, sample_rows, to_dev,
+                        to_dev_bf16, y_tolerance_ok)
+
+pytestmark = pytest.mark.gpu
+
+
+def _q_planes_from_dev(q, layout, M, K):
+    q = q.cpu().numpy()
+    if layout == S.SEGQ_Q_SIGNED:
+        q = q[:, :K]
+        return np.maximum(q, 0).astype(np.int8), np.minimum(q, 0).astype(np.int8)
+    return q[0, :, :K].copy(), q[1, :, :K].copy()
+
+
+# ----------------------------------------------------- activation side ----
+ACT_CASES = [
+    # M, K, kseg, kind
+    (1, 64, [64], "gelu"),
+    (37, 192, [64, 128], "blocks"),
+    (300, 512, [64] * 8, "blocks"),
+    (129, 1536, [1536], "silu"),
+    (64, 1000, [512, 488], "gelu"),      # ragged K (last segment not 64-aligned)
+    (5, 8200, [4096, 4104], "normal"),
+    (17, 256, [256], "pos"),
+    (17, 256, [256], "neg"),
+]
+
+
+@pytest.mark.parametrize("M,K,kseg,kind", ACT_CASES)
+def test_calibrate_and_quantize_bitexact(M, K, kseg, kind):
+    x, _ = W.make_custom(M, K, 16, seed=M + K, kind=kind, x_scale=2.0)
+    ref_scales = np.stack(oracle.calibrate_amax(x, kseg))
+    xd = to_dev_bf16(x)
+    act = S.segquant_calibrate_amax(xd, kseg)
+    assert np.array_equal(act.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
+    qp, qn = oracle.quantize_dualscale(x, kseg, ref_scales[2], ref_scales[3])
+    for layout in (S.SEGQ_Q_SIGNED, S.SEGQ_Q_PLANES):
+        q = S.segquant_quantize_dualscale(xd, act, kseg, layout)
+        gp, gn = _q_planes_from_dev(q, layout, M, K)
+        assert np.array_equal(gp, qp), f"q+ mismatch layout {layout}"
+        assert np.array_equal(gn, qn), f"q- mismatch layout {layout}"
+
+
+def test_calibrate_and_quantize_ragged_row_in_padded_buffer():
+    """K = 1003 (not a multiple of 8) inside rows padded to 1008: the last
+    partial 8-element piece is handled element by element, padding ignored."""
+    import torch
+    M, K = 9, 1003
+    x, _ = W.make_custom(M, K, 16, seed=11, kind="gelu", x_scale=3.0)
+    kseg = [512, 491]
+    ref = np.stack(oracle.calibrate_amax(x, kseg))
+    qp, qn = oracle.quantize_dualscale(x, kseg, ref[2], ref[3])
+    pad = np.full((M, 1008), W.f32_to_bf16_bits(np.array([50.0], np.float32))[0], np.uint16)
+    pad[:, :K] = x
+    xd = to_dev_bf16(pad)[:, :K]
+    act = S.segquant_calibrate_amax(xd, kseg)
+    assert np.array_equal(act.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    for layout in (S.SEGQ_Q_SIGNED, S.SEGQ_Q_PLANES):
+        q = S.segquant_quantize_dualscale(xd, act, kseg, layout)
+        gp, gn = _q_planes_from_dev(q, layout, M, K)
+        assert np.array_equal(gp, qp) and np.array_equal(gn, qn)
+
+
+def test_quantize_saturates_static_scales_and_infinities():
+    """Scales calibrated on one batch, applied to a batch with larger values
+    and +-Inf: codes clamp at the ends of each half's range."""
+    calib, _ = W.make_custom(16, 128, 16, seed=1, kind="normal")
+    x = W.f32_to_bf16_bits(W.bf16_bits_to_f32(calib) * np.float32(3.0))
+    x[0, :4] = W.f32_to_bf16_bits(np.array([np.inf, -np.inf, 1e30, -1e30], np.float32))
+    sc = np.stack(oracle.calibrate_amax(calib, [128]))
+    qp, qn = oracle.quantize_dualscale(x, [128], sc[2], sc[3])
+    act = S.segquant_calibrate_amax(to_dev_bf16(calib), [128])
+    q = S.segquant_quantize_dualscale(to_dev_bf16(x), act, [128], S.SEGQ_Q_PLANES)
+    gp, gn = _q_planes_from_dev(q, S.SEGQ_Q_PLANES, 16, 128)
+    assert np.array_equal(gp, qp) and np.array_equal(gn, qn)
+    assert gp[0, :4].tolist() == [127, 0, 127, 0] and gn[0, :4].tolist() == [0, -128, 0, -128]
+
+
+# -------------------------------------------------------- weight side ----
+W_CASES = [
+    # K, N, kseg, nseg, per_column
+    (64, 16, [64], [16], False),
+    (256, 768, [256], [256, 256, 256], False),
+    (192, 48, [64, 128], None, True),
+    (1536, 1536, [64] * 24, [1536], False),
+    (640, 272, [128, 512], [16, 256], False),
+]
+
+
+@pytest.mark.parametrize("K,N,kseg,nseg,per_column", W_CASES)
+def test_weight_quantize_pack_bitexact(K, N, kseg, nseg, per_column):
+    g = np.random.default_rng(K + N)
+    w = (g.standard_normal((K, N)) * np.exp(g.uniform(-3, 0, N))[None, :]).astype(np.float32)
+    wq, ws = oracle.quantize_weight(w, kseg, nseg, per_column)
+    wp, gws = S.segquant_quantize_weight(to_dev(w), kseg, nseg, per_column)
+    assert np.array_equal(gws.cpu().numpy().view(np.uint32), ws.view(np.uint32))
+    assert np.array_equal(S.segquant_unpack_weight(wp, K, N).cpu().numpy(), wq)
+
+
+# ---------------------------------------------------------------- GEMM ----
+GEMM_CASES = [
+    # M, K, N, kseg, nseg, per_column, kind
+    (1, 64, 16, [64], [16], False, "gelu"),
+    (2, 1536, 576, [1536], [96] * 6, False, "silu"),
+    (3, 256, 48, [64, 192], None, True, "blocks"),
+    (16, 640, 256, [64] * 10, [256], False, "blocks"),
+    (17, 256, 272, [256], None, True, "gelu"),
+    (77, 384, 768, [128, 256], [256] * 3, False, "gelu"),
+    (200, 1536, 1536, [64] * 24, [1536], False, "blocks"),
+    (333, 512, 320, [512], None, True, "gelu"),
+    (257, 1024, 528, [256] * 4, [528], False, "gelu"),
+    (130, 704, 64, [64, 128, 512], [32, 32], False, "normal"),
+    (64, 256, 768, [256], [256, 256, 256], False, "pos"),
+    (64, 256, 256, [128, 128], None, True, "neg"),
+]
+
+
+def _ids(c):
+    return f"M{c[0]}_K{c[1]}_N{c[2]}_S{len(c[3])}_{c[6]}"
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=[_ids(c) for c in GEMM_CASES])
+@pytest.mark.parametrize("mode", ["bf16", "signed", "planes"])
+def test_gemm_parity(case, mode):
+    import torch
+    M, K, N, kseg, nseg, per_column, kind = case
+    x, w = W.make_custom(M, K, N, seed=M * 7 + K + N, kind=kind, x_scale=2.0)
+    ref = OracleLayer(x, w, kseg, nseg, per_column)
+    gpu = GpuLayer(x, w, kseg, nseg, per_column)
+    assert np.array_equal(gpu.act.cpu().numpy().view(np.uint32), ref.act.view(np.uint32))
+    flag_sets = [S.SEGQ_GEMM_FORCE_TILE]
+    if M <= 16:
+        flag_sets.append(S.SEGQ_GEMM_FORCE_SMALLM)
+    for flags in flag_sets:
+        y, acc = gpu.run(mode, flags=flags, debug=True)
+        assert np.array_equal(acc.cpu().numpy(), ref.acc), f"int32 accumulators, flags {flags}"
+        ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), ref.y)
+        assert ok, f"bf16 Y out of tolerance (flags {flags}): {nbad} elements, worst excess {worst}"
+        # the production variant (no accumulator dump) gives the same Y
+        y2, _ = gpu.run(mode, flags=flags, debug=False)
+        assert torch.equal(y2, y)
+
+
+def test_gemm_empty_batch_is_a_noop():
+    import torch
+    x, w = W.make_custom(4, 128, 32, seed=3)
+    gpu = GpuLayer(x, w, [128], [32], False)
+    empty = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    y = S.segquant_gemm_w8a8_seg(empty, gpu.wp, gpu.ws, gpu.act, [128])
+    assert tuple(y.shape) == (0, 32)
+
+
+def test_gemm_does_not_write_outside_its_rows():
+    """Rows of a larger Y buffer outside [0, M) and columns beyond N keep
+    their contents (guard bands)."""
+    import torch
+    M, K, N = 77, 256, 272
+    x, w = W.make_custom(M, K, N, seed=5, kind="gelu")
+    ref = OracleLayer(x, w, [256], None, True)
+    gpu = GpuLayer(x, w, [256], None, True)
+    for flags in (S.SEGQ_GEMM_FORCE_TILE,):
+        big = torch.full((M + 3, N + 32), 7.0, dtype=torch.bfloat16, device=DEV)
+        out = big[1:M + 1, :N]
+        S.segquant_gemm_w8a8_seg(gpu.xd, gpu.wp, gpu.ws, gpu.act, [256], out=out, flags=flags)
+        torch.cuda.synchronize()
+        b = big.float().cpu().numpy()
+        assert np.all(b[0] == 7.0) and np.all(b[M + 1:] == 7.0) and np.all(b[:, N:] == 7.0)
+        ok, worst, nbad = y_tolerance_ok(b[1:M + 1, :N].astype(np.float64), ref.y)
+        assert ok
+
+
+# ------------------------------------------- full-size named workloads ----
+@pytest.mark.parametrize("name", W.ORDER)
+def test_full_size_workload(name):
+    """At the workloads' full sizes and in the configuration the benchmark
+    times: scales, packed weights bit-exact; int32 accumulators and Y on
+    sampled rows (first, last -- the ragged row tile -- and random)."""
+    import torch
+    wl, x, w = W.make_inputs(name)
+    nseg = None if wl.per_column else list(wl.nseg)
+    rows = sample_rows(wl.M, 24) if wl.M > 64 else np.arange(wl.M)
+    ref = OracleLayer(x, w, wl.kseg, nseg, wl.per_column, rows=rows, with_acc=True)
+    gpu = GpuLayer(x, w, wl.kseg, nseg, wl.per_column)
+    assert np.array_equal(gpu.act.cpu().numpy().view(np.uint32), ref.act.view(np.uint32))
+    assert np.array_equal(gpu.ws.cpu().numpy().view(np.uint32), ref.ws.view(np.uint32))
+    assert np.array_equal(S.segquant_unpack_weight(gpu.wp, wl.K, wl.N).cpu().numpy(), ref.wq)
+    y, _ = gpu.run("bf16", debug=False)
+    ymax = float(np.abs(ref.y).max())
+    ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y)[rows], ref.y, ymax)
+    assert ok, f"{name}: {nbad} sampled outputs out of tolerance, worst excess {worst}"
+    yd, acc = gpu.run("bf16", debug=True)
+    ridx = torch.from_numpy(rows).to(DEV)
+    acc_rows = acc.index_select(2, ridx).cpu().numpy()
+    assert np.array_equal(acc_rows, ref.acc), f"{name}: int32 accumulators differ"
+    assert torch.equal(yd, y)

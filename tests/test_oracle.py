@@ -108,6 +108,21 @@ def test_zero_range_gives_zero_half(kind, zero_half):
         assert sp[0] == 0 and ip[0] == 0 and not qp.any() and qn.min() == -128
 
 
+def test_range_too_small_for_an_fp32_inverse_counts_as_zero():
+    """127/a overflows fp32 for a below about 3.7e-37: such a range is
+    treated like a zero range (s = inv = 0, codes 0), for activations and
+    weights alike."""
+    x = bits(np.array([[1e-38, -2.0, 0.0]], np.float32))
+    sp, sn, ip, ineg = oracle.calibrate_amax(x, [3])
+    assert (sp[0], ip[0]) == (0.0, 0.0) and sn[0] == np.float32(2.0 / 128)
+    qp, qn = oracle.quantize_dualscale(x, [3], ip, ineg)
+    assert qp.tolist() == [[0, 0, 0]] and qn.tolist() == [[0, -128, 0]]
+    w = np.array([[1e-38, -1e-38], [0.0, 2.0]], np.float32)
+    wq, ws = oracle.quantize_weight(np.repeat(w, 32, axis=0), [64], None, per_column=True)
+    assert ws[0, 0] == 0 and not wq[:, 0].any()
+    assert ws[0, 1] == np.float32(2.0 / 127) and wq[:, 1].min() == 0 and wq[:, 1].max() == 127
+
+
 def test_signed_zero_and_subnormals():
     x = bits(np.array([[0.0, -0.0, 1e-40, -1e-40, 3.0, -3.0]], np.float32))
     sp, sn, ip, ineg = oracle.calibrate_amax(x, [6])
