@@ -13,6 +13,7 @@ namespace sq {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 // 1.5 * 2^23: adding it to a float v with |v| < 2^22 rounds v to the nearest
 // integer, ties to even (the sum lands where the fp32 spacing is exactly 1
