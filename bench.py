@@ -10,15 +10,29 @@ static scales and the packed weights are prepared before timing (offline in
 the method).  Inputs are resident in HBM; R copies of them rotate so that no
 cache (4 MB L2 per XCD, 256 MB MALL) holds a step's operands from the step
 before.  The timed steps are replayed from a captured HIP graph (one graph of
-R calls), bracketed by events and device synchronisation.
+R calls) on a stream of our own, bracketed by HIP events on that stream and
+device synchronisation.
 
 Prints ONE JSON line.  `value` is the workload's metric: GB/s of algorithmic
 bytes (bf16 X + int8 W + bf16 Y) for the small-M AdaNorm layer (HBM bound),
-effective TOPS (4*M*N*K int8 ops: both polarity halves) otherwise.
+effective TOPS (4*M*N*K int8 ops: both polarity halves) otherwise.  The line
+also carries the roofline of the kernel (with the HBM traffic measured by
+rocprofv3 counters when a counter record of the current kernel source exists
+under profiles/), the CPU oracle timed on a bounded sample, and the same
+measurement for every named workload ("all_workloads").
+
+Counter passes (run under rocprofv3 --pmc, one counter per run):
+    python bench.py --workload NAME --pmc-pass
+runs a few plain (non-graph) steps and then a copy of known size (the scale
+of the byte counters).  --ingest-pmc FETCH_DIR WRITE_DIR turns the two runs'
+CSV output into the counter record profiles/traffic_<kernel>_<workload>.txt.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -34,6 +48,17 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix (5.0 POP/s)
 METRIC = "DualScale seg-W8A8 GEMM effective TOPS & % int8 MFMA peak; GB/s at small M"
 DEFAULT_WORKLOAD = "c2_adanorm_gemv"
+COPY_PROBE_BYTES = 256 << 20
+CSRC = os.path.join(ROOT, "segmented_dual_scale_amd", "csrc")
+KERNEL_SOURCES = {
+    "gemm_smallm_kernel": ["gemm_smallm.hip", "sq_device.hpp", "sq_launch.hpp"],
+    "gemm_tile_kernel": ["gemm_tile.hip", "sq_device.hpp", "sq_launch.hpp"],
+}
+# The pages' own timing figures: whole-model, per denoising step, not per layer.
+PAGES_LATENCY = ("hliangzhao.me 'SegQuant' page, deployment-cost table (SD3.5 on an RTX 4090, "
+                 "whole backbone per sampling step): FP16 317.18 ms, INT8 baseline 278.86 ms, "
+                 "SegQuant-8 287.85 ms, INT4 baseline 209.78 ms, SegQuant-4 212.87 ms; the "
+                 "pages give no per-layer or per-kernel latency")
 
 
 def alg_bytes(wl) -> int:
@@ -47,6 +72,42 @@ def alg_ops(wl) -> int:
 def hbm_bound(wl) -> bool:
     # ridge of MI355X: 5.0e15 ops / 8.0e12 B/s = 625 ops per byte
     return alg_ops(wl) / alg_bytes(wl) < 625.0
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_record_path(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+
+
+def read_traffic(kernel: str, workload: str, mode: str):
+    """HBM bytes per launch from the counter record, or None when there is no
+    record for this kernel source (the kernel changed since it was taken)."""
+    path = traffic_record_path(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ln.startswith("#") or ":" not in ln:
+                continue
+            k, v = ln.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != source_digest(kernel) or rec.get("mode") != mode:
+        return None
+    fetch_f = float(rec["copy_fetch_kib"]) * 1024 / float(rec["copy_bytes"])
+    write_f = float(rec["copy_write_kib"]) * 1024 / float(rec["copy_bytes"])
+    fetch = float(rec["fetch_kib_per_dispatch"]) * 1024 / fetch_f
+    write = float(rec["write_kib_per_dispatch"]) * 1024 / write_f
+    return {"bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+            "copy_scale_fetch": fetch_f, "copy_scale_write": write_f,
+            "record": os.path.relpath(path, ROOT)}
 
 
 def cpu_baseline(wl, x, w, seconds: float = 12.0):
@@ -69,7 +130,7 @@ def cpu_baseline(wl, x, w, seconds: float = 12.0):
         t0 = time.perf_counter()
         oracle.dualscale_linear(xs, wq, ws, list(wl.kseg), sp, sn, ip, ineg)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() > t_end or len(times) >= 50:
+        if time.perf_counter() > t_end or len(times) >= 10000:
             break
     t = statistics.median(times)
     sub = wl.__class__(wl.name, wl.index, rows, wl.K, wl.N, wl.kseg, wl.nseg, wl.per_column)
@@ -80,8 +141,187 @@ def cpu_baseline(wl, x, w, seconds: float = 12.0):
     return {"value": value, "unit": unit, "cores": min(threads, rows), "kind": "oracle",
             "sample": f"{rows} of {wl.M} rows (full K={wl.K}, N={wl.N}), median of {len(times)} "
                       f"calls of oracle_dualscale_linear (quantise, exact int32 products, fp64 "
-                      f"dequantise); calibration and weight quantisation not timed",
+                      f"dequantise) over {sum(times):.1f} s; calibration and weight "
+                      f"quantisation not timed",
             "seconds_per_call": t}
+
+
+class Layer:
+    """One workload's operands on the GPU, R rotating copies."""
+
+    def __init__(self, S, W, dev, name: str, mode: str, rotate: bool = True):
+        import numpy as np
+        import torch
+        self.S, self.mode = S, mode
+        wl, x, w = W.make_inputs(name)
+        self.wl, self.x, self.w = wl, x, w
+        self.kseg = list(wl.kseg)
+        nseg = None if wl.per_column else list(wl.nseg)
+        # offline: calibration + weight quantisation (not timed)
+        xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.act = S.segquant_calibrate_amax(xd, self.kseg)
+        wd = torch.from_numpy(w).to(dev)
+        wp, self.ws = S.segquant_quantize_weight(wd, self.kseg, nseg, wl.per_column)
+        del wd
+        self.layout = {"signed": S.SEGQ_Q_SIGNED, "planes": S.SEGQ_Q_PLANES}.get(mode)
+        xq = S.segquant_quantize_dualscale(xd, self.act, self.kseg, self.layout) \
+            if self.layout is not None else None
+        torch.cuda.synchronize()
+        R = max(1, min(64, math.ceil(640e6 / alg_bytes(wl)))) if rotate else 1
+        self.R = R
+        if xq is None:
+            self.xs = [xd] + [xd.clone() for _ in range(R - 1)]
+            self.xqs = [None] * R
+        else:
+            del xd
+            self.xs = [None] * R
+            self.xqs = [xq] + [xq.clone() for _ in range(R - 1)]
+        self.wps = [wp] + [wp.clone() for _ in range(R - 1)]
+        self.ys = [torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        torch.cuda.synchronize()
+        kid = S.segquant_gemm_kernel_for(wl.M, wl.N, wl.K)
+        self.kernel = "gemm_smallm_kernel" if kid == S.SEGQ_KERNEL_SMALLM else "gemm_tile_kernel"
+
+    def step(self, i: int):
+        S, j = self.S, i % self.R
+        if self.layout is None:
+            S.segquant_gemm_w8a8_seg(self.xs[j], self.wps[j], self.ws, self.act, self.kseg,
+                                     out=self.ys[j])
+        else:
+            S.segquant_gemm_w8a8_seg(None, self.wps[j], self.ws, self.act, self.kseg,
+                                     N=self.wl.N, xq=self.xqs[j], q_layout=self.layout,
+                                     out=self.ys[j])
+
+    def time(self, stream, steps: int, warmup: int, use_graph: bool, min_seconds: float = 0.0):
+        """Average ms per step over >= `steps` timed steps (whole graph replays)."""
+        import torch
+        R = self.R
+        with torch.cuda.stream(stream):
+            for i in range(max(warmup, R)):
+                self.step(i)
+        torch.cuda.synchronize()
+        graph = None
+        if use_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(R):
+                    self.step(i)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                for _ in range(max(1, warmup // R)):
+                    graph.replay()
+            torch.cuda.synchronize()
+            reps = max(1, math.ceil(steps / R))
+            if min_seconds > 0:  # size the timed region from one timed replay
+                t0 = time.perf_counter()
+                with torch.cuda.stream(stream):
+                    graph.replay()
+                torch.cuda.synchronize()
+                reps = max(reps, math.ceil(min_seconds / max(time.perf_counter() - t0, 1e-6)))
+            n = reps * R
+        else:
+            n = steps
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            if use_graph:
+                for _ in range(n // R):
+                    graph.replay()
+            else:
+                for i in range(n):
+                    self.step(i)
+            end.record(stream)
+        torch.cuda.synchronize()
+        del graph
+        return start.elapsed_time(end) / n, n
+
+    def metrics(self, ms_per_step: float):
+        wl = self.wl
+        if hbm_bound(wl):
+            v = alg_bytes(wl) / (ms_per_step * 1e-3) / 1e9
+            return {"value": v, "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
+                    "frac": v / PEAK_HBM_GBS}
+        v = alg_ops(wl) / (ms_per_step * 1e-3) / 1e12
+        return {"value": v, "unit": "TOPS", "bound": "mfma", "peak": PEAK_INT8_TOPS,
+                "frac": v / PEAK_INT8_TOPS}
+
+    def free(self):
+        self.xs = self.xqs = self.wps = self.ys = None
+
+
+def copy_probe(dev, reps: int = 3):
+    """A copy of known size (the scale of the FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+    src = torch.randint(0, 1 << 30, (COPY_PROBE_BYTES // 4,), dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _counter_means(run_dir: str, name_part: str):
+    """Mean per dispatch of each counter over kernels whose name contains name_part."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if name_part not in r["Kernel_Name"]:
+                    continue
+                key = (f, r["Dispatch_Id"])
+                d = per.setdefault(r["Counter_Name"], {})
+                d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
+    return {c: (sum(d.values()) / len(d), len(d)) for c, d in per.items()}
+
+
+def ingest_pmc(fetch_dir: str, write_dir: str, workload: str, mode: str, kernel: str,
+               command: str):
+    f_k = _counter_means(fetch_dir, kernel)["FETCH_SIZE"]
+    w_k = _counter_means(write_dir, kernel)["WRITE_SIZE"]
+    f_c = _counter_means(fetch_dir, "bitwise_not")["FETCH_SIZE"]
+    w_c = _counter_means(write_dir, "bitwise_not")["WRITE_SIZE"]
+    path = traffic_record_path(kernel, workload)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        fh.write(f"# HBM traffic of {kernel} on {workload} ({mode} activation input), from\n"
+                 f"# rocprofv3 counters, one counter per run (mean over dispatches):\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            fh.write(f"#   rocprofv3 --pmc {c} -d <dir> -o pmc --output-format csv -- {command}\n")
+        fh.write(f"# The copy probe is torch.bitwise_not over {COPY_PROBE_BYTES} bytes of int32\n"
+                 f"# (reads and writes that many bytes): its counters give the KiB scale.\n"
+                 f"# source_sha256 covers {', '.join(KERNEL_SOURCES[kernel])}.\n")
+        fh.write(f"kernel: {kernel}\nworkload: {workload}\nmode: {mode}\n")
+        fh.write(f"source_sha256: {source_digest(kernel)}\n")
+        fh.write(f"fetch_kib_per_dispatch: {f_k[0]:.1f}\n")
+        fh.write(f"write_kib_per_dispatch: {w_k[0]:.1f}\n")
+        fh.write(f"dispatches: {f_k[1]} {w_k[1]}\n")
+        fh.write(f"copy_bytes: {COPY_PROBE_BYTES}\n")
+        fh.write(f"copy_fetch_kib: {f_c[0]:.1f}\n")
+        fh.write(f"copy_write_kib: {w_c[0]:.1f}\n")
+    print(open(path).read())
+
+
+def summarize_trace(run_dir: str):
+    """Per-kernel duration statistics of a rocprofv3 --kernel-trace run (CSV output)."""
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {run_dir}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                per.setdefault(r["Kernel_Name"], []).append(
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print(f"{'calls':>7} {'mean_us':>10} {'p10_us':>10} {'median_us':>10} {'p90_us':>10}  kernel")
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        v.sort()
+        n = len(v)
+        print(f"{n:7d} {sum(v) / n / 1e3:10.2f} {v[n // 10] / 1e3:10.2f} {v[n // 2] / 1e3:10.2f} "
+              f"{v[(9 * n) // 10] / 1e3:10.2f}  {name[:150]}")
 
 
 def main():
@@ -95,14 +335,32 @@ def main():
                          "an activation pre-quantised by segquant_quantize_dualscale")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch each step from Python")
+    ap.add_argument("--no-all", action="store_true", help="skip the all_workloads summary")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="a few plain steps of --workload, then the copy probe (run under "
+                         "rocprofv3 --pmc)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print per-kernel duration statistics of a rocprofv3 kernel trace")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the counter record of --workload from two --pmc-pass runs")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.ingest_pmc:
+        import segmented_dual_scale_amd.workloads as W
+        wl = W.WORKLOADS[args.workload]
+        kernel = "gemm_smallm_kernel" if wl.M <= 16 else "gemm_tile_kernel"
+        cmd = f"python3 bench.py --workload {args.workload} --mode {args.mode} --pmc-pass"
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload, args.mode, kernel, cmd)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer is a single-GPU kernel library and this "
               "build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import segmented_dual_scale_amd as S
@@ -113,91 +371,42 @@ def main():
         sys.exit(2)
     S.load_library()
     dev = torch.device("cuda:0")
-    wl, x, w = W.make_inputs(args.workload)
-    kseg = list(wl.kseg)
-    nseg = None if wl.per_column else list(wl.nseg)
-
-    # ---- offline: calibration + weight quantisation (not timed) ----
-    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-    act = S.segquant_calibrate_amax(xd, kseg)
-    wd = torch.from_numpy(w).to(dev)
-    wp, ws = S.segquant_quantize_weight(wd, kseg, nseg, wl.per_column)
-    del wd
-    layout = {"signed": S.SEGQ_Q_SIGNED, "planes": S.SEGQ_Q_PLANES}.get(args.mode)
-    xq = S.segquant_quantize_dualscale(xd, act, kseg, layout) if layout is not None else None
-    torch.cuda.synchronize()
-
-    # ---- rotating copies so no cache serves the operands ----
-    set_bytes = alg_bytes(wl)
-    R = max(1, min(64, math.ceil(640e6 / set_bytes)))
-    xs = [xd] + [xd.clone() for _ in range(R - 1)]
-    xqs = [xq] + [xq.clone() for _ in range(R - 1)] if xq is not None else [None] * R
-    wps = [wp] + [wp.clone() for _ in range(R - 1)]
-    ys = [torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-    torch.cuda.synchronize()
-
-    def step(i):
-        j = i % R
-        if xq is None:
-            S.segquant_gemm_w8a8_seg(xs[j], wps[j], ws, act, kseg, out=ys[j])
-        else:
-            S.segquant_gemm_w8a8_seg(None, wps[j], ws, act, kseg, N=wl.N, xq=xqs[j],
-                                     q_layout=layout, out=ys[j])
-
     stream = torch.cuda.Stream(device=dev)  # default priority
-    use_graph = not args.no_graph
-    with torch.cuda.stream(stream):
-        for i in range(max(args.warmup, R)):
-            step(i)
-    torch.cuda.synchronize()
-    graph = None
-    if use_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(R):
-                step(i)
-        torch.cuda.synchronize()
+
+    if args.pmc_pass:
+        layer = Layer(S, W, dev, args.workload, args.mode, rotate=False)
         with torch.cuda.stream(stream):
-            for _ in range(max(1, args.warmup // R)):
-                graph.replay()
+            for i in range(8):
+                layer.step(i)
         torch.cuda.synchronize()
+        layer.free()
+        copy_probe(dev)
+        print(f"pmc pass done: {layer.kernel} on {args.workload}, 8 dispatches; copy probe "
+              f"{COPY_PROBE_BYTES} bytes", flush=True)
+        return
 
-    reps = max(1, math.ceil(args.steps / R)) if use_graph else 0
-    steps = reps * R if use_graph else args.steps
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        if use_graph:
-            for _ in range(reps):
-                graph.replay()
-        else:
-            for i in range(steps):
-                step(i)
-        end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = start.elapsed_time(end)
-    ms_per_step = ms_total / steps
-
-    if hbm_bound(wl):
-        unit, value = "GB/s", alg_bytes(wl) / (ms_per_step * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": value, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": value / PEAK_HBM_GBS, "traffic": None}
-    else:
-        unit, value = "TOPS", alg_ops(wl) / (ms_per_step * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": value, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
-                "frac": value / PEAK_INT8_TOPS, "traffic": None}
-    kernel = "gemm_smallm_kernel" if S.segquant_gemm_kernel_for(wl.M, wl.N, wl.K) == \
-        S.SEGQ_KERNEL_SMALLM else "gemm_tile_kernel"
-    roof["kernel"] = kernel
-    roof["per_launch"] = {"alg_bytes": alg_bytes(wl), "alg_int8_ops": alg_ops(wl),
-                          "avg_us": ms_per_step * 1e3}
+    use_graph = not args.no_graph
+    layer = Layer(S, W, dev, args.workload, args.mode)
+    wl = layer.wl
+    ms_per_step, steps = layer.time(stream, args.steps, args.warmup, use_graph)
+    m = layer.metrics(ms_per_step)
+    roof = {"bound": m["bound"], "achieved": m["value"], "peak": m["peak"], "unit": m["unit"],
+            "frac": m["frac"], "traffic": None, "kernel": layer.kernel,
+            "per_launch": {"alg_bytes": alg_bytes(wl), "alg_int8_ops": alg_ops(wl),
+                           "avg_us": ms_per_step * 1e3}}
+    tr = read_traffic(layer.kernel, wl.name, args.mode)
+    if tr is not None:
+        roof["traffic"] = tr["bytes_per_launch"]
+        roof["traffic_unit"] = "bytes per launch"
+        roof["traffic_detail"] = tr
+    R = layer.R
+    x_host, w_host = layer.x, layer.w
+    layer.free()
+    del layer
+    torch.cuda.empty_cache()
 
     line = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
+        "metric": METRIC, "value": m["value"], "unit": m["unit"], "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic (seeded generators with the workload's shapes and polarity structure)",
@@ -207,10 +416,23 @@ def main():
                    "rotating_sets": R, "hip_graph": use_graph,
                    "useful_2mnk_tops": alg_ops(wl) / 2 / (ms_per_step * 1e-3) / 1e12},
         "roofline": roof,
-        "wall_s": wall,
+        "pages_latency": PAGES_LATENCY,
     }
+    if not args.no_all:
+        summary = {}
+        for name in W.ORDER:
+            lay = Layer(S, W, dev, name, args.mode)
+            ms, n = lay.time(stream, 1, 10, use_graph, min_seconds=0.05)
+            mm = lay.metrics(ms)
+            summary[name] = {"value": mm["value"], "unit": mm["unit"], "bound": mm["bound"],
+                             "frac": mm["frac"], "us_per_step": ms * 1e3, "steps": n,
+                             "kernel": lay.kernel, "M": lay.wl.M, "K": lay.wl.K, "N": lay.wl.N}
+            lay.free()
+            del lay
+            torch.cuda.empty_cache()
+        line["all_workloads"] = summary
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, x, w)
+        line["cpu_baseline"] = cpu_baseline(wl, x_host, w_host)
     print(json.dumps(line), flush=True)
 
 
