@@ -10,17 +10,25 @@
 // [P2] "SegQuant" (hliangzhao.me): section 1 (AdaNorm emits shift, scale
 //      and gate for two branches), section 3 (reconstruction).
 //
-// Design: each wave owns one 16-column n-tile and walks all of K.  The
-// packed weight keeps an n-tile's K as consecutive 1 KiB tiles, so a wave's
-// weight stream is one contiguous range read with one 16-byte load per lane
-// per tile -- the matrix-core B operand as loaded.  A wave requests up to
-// kRing tiles before doing anything else, so for K <= 2048 the whole weight
-// is in flight from the first instructions; the workgroup meanwhile
-// quantises X (M rows, a chunk of K at a time) into two LDS planes.  Rows of
-// the 16-row A operand at or beyond M are zero.  Both halves run on the int8
-// 16x16x64 matrix cores against the same B registers (the padding rows cost
-// nothing: the kernel is bound by HBM).  Index math uses shifts only; the
-// scale table is staged once in LDS.
+// Each wave owns one 16-column n-tile and walks all of K.  The packed weight
+// keeps an n-tile's K as consecutive 1 KiB tiles, so a wave's weight stream
+// is one contiguous range, one 16-byte load per lane per tile -- the
+// matrix-core B operand as loaded.  Rows of the 16-row A operand at or beyond
+// M are zero; both halves run on the int8 16x16x64 matrix cores against the
+// same B registers (the padding rows cost nothing: the kernel is bound by
+// HBM).
+//
+// Two kernels:
+//   gemm_smallm_kernel          K <= 2048 and X small enough to stage in
+//                               registers (the AdaNorm shapes): every load
+//                               of the call is issued up front, small ones
+//                               first, so the tables and X never queue
+//                               behind the weight stream; then quantise
+//                               into LDS, fetch every A fragment, and run
+//                               the matrix-core chain as the weight tiles
+//                               arrive.
+//   gemm_smallm_chunked_kernel  any other small-M shape: K in chunks that fit
+//                               LDS, a ring of weight tiles kept ahead.
 #include "sq_device.hpp"
 #include "sq_launch.hpp"
 
@@ -56,7 +64,7 @@ struct SmallArgs {
 // ONE: all of K is one chunk that fits the weight ring (no refills, no
 // chunk loop: straight-line code with an exact count of loads in flight).
 template <int WPG, int QL, bool ONE, bool DEBUG>
-__global__ __launch_bounds__(64 * WPG) void gemm_smallm_kernel(SmallArgs a) {
+__global__ __launch_bounds__(64 * WPG) void gemm_smallm_chunked_kernel(SmallArgs a) {
   constexpr int NTHR = 64 * WPG;
   __shared__ __attribute__((aligned(16))) uint8_t xs[kXBytes];
   __shared__ float inv_tab[2 * kMaxKSeg];
@@ -218,9 +226,311 @@ __global__ __launch_bounds__(64 * WPG) void gemm_smallm_kernel(SmallArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Streaming kernel (K <= 2048).
+
+// An empty use of a loaded value.  Placed after the weight stream has been
+// issued, it keeps an earlier load where it was written: a load whose only
+// use sits in a branch may otherwise be sunk into that branch, behind the
+// weight stream, and then wait for all of it.  (The wait it implies is for
+// loads issued before the weights, which are needed next anyway.)
+template <typename T>
+__device__ __forceinline__ void pin_load(const T &v) {
+  asm volatile("" ::"v"(v));
+}
+
+constexpr int kStreamThreads = 256;  // 4 waves, one n-tile each
+constexpr int kStreamXR = 8;         // 16-byte X pieces staged per thread
+constexpr int kStreamMaxKT = 32;     // k-tiles (K <= 2048)
+constexpr int kStreamPitch = kStreamMaxKT * 64 + 16;
+constexpr int kStreamPre = 4;        // segments whose weight scales are fetched up front
+
+struct StreamArgs {
+  int32_t M, N, K;
+  int32_t pieces_per_row;  // 16-byte pieces per input row (bf16: K/8, int8: K/16)
+  int32_t pieces;          // M * pieces_per_row
+  uint32_t ppr_magic;      // ceil(2^32 / pieces_per_row): row = umulhi(piece, magic), exact
+                           // for pieces < 4096 and pieces_per_row <= 4096
+  const uint8_t *x;        // bf16 X, signed codes, or the + plane
+  int64_t ld_bytes;        // row stride of x in bytes
+  int64_t plane_stride;    // bytes from the + plane to the - plane (planes input)
+  const int8_t *w;
+  const float *w_scale;
+  const float *act;  // [4][n_kseg]
+  uint16_t *y;
+  int64_t ld_y;
+  int32_t *acc;
+  int32_t n_kseg;      // <= kStreamMaxKT (every segment is whole k-tiles)
+  uint32_t fold_mask;  // bit t: a K-segment ends with k-tile t
+};
+
+// QL: activation input, -1 bf16 (quantised here), 0 signed codes, 1 planes.
+// RING: weight tiles requested per wave, a multiple of 8 with K/64 <= RING.
+// SEG1: the call has one K-segment.
+template <int QL, int RING, bool SEG1, bool DEBUG>
+__global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t planes[2 * kSmallMMax * kStreamPitch];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int NT = a.N / 16, KT = a.K / 64, nS = a.n_kseg;
+  const int nt = blockIdx.x * 4 + wave;
+  const bool active = nt < NT;
+  const int ntc = min(nt, NT - 1);  // idle waves work on a valid tile and store nothing
+  const int n = ntc * 16 + (lane & 15);
+  const int pitch = a.K + 16;
+  uint8_t *pp = planes;
+  uint8_t *pn = planes + a.M * pitch;
+
+  // (1) this thread's pieces of X and, for bf16 input, the inverse scales of
+  //     their segments (the segment of k-tile kt is the number of segment
+  //     ends before it).  Pieces past the end load a valid piece and are
+  //     never stored.  These go first: what is issued after the weight
+  //     stream waits behind it.
+  v4u xr[kStreamXR], xn[QL == 1 ? kStreamXR : 1];
+  float ipv[QL < 0 ? kStreamXR : 1], inv_[QL < 0 ? kStreamXR : 1];
+#pragma unroll
+  for (int i = 0; i < kStreamXR; ++i) {
+    const int pc = min(tid + i * kStreamThreads, a.pieces - 1);
+    const int row = (int)__umulhi((uint32_t)pc, a.ppr_magic), c = pc - row * a.pieces_per_row;
+    const uint8_t *src = a.x + row * a.ld_bytes + c * 16;
+    xr[i] = *reinterpret_cast<const v4u *>(src);
+    if (QL == 1) xn[QL == 1 ? i : 0] = *reinterpret_cast<const v4u *>(src + a.plane_stride);
+    if (QL < 0) {
+      const int sg = __builtin_popcount(a.fold_mask & ((1u << (c >> 3)) - 1u));
+      ipv[QL < 0 ? i : 0] = a.act[2 * nS + sg];
+      inv_[QL < 0 ? i : 0] = a.act[3 * nS + sg];
+    }
+  }
+
+  // (2) what the folds need: this lane's segment pair s+/s- (lane i holds
+  //     segment i) and the weight scales of the first kStreamPre segments for
+  //     column n (a queue: each fold takes the head and fetches one more)
+  const int ti = min(lane & 31, nS - 1);
+  const float sp_l = a.act[ti];
+  const float sn_l = a.act[nS + ti];
+  float wsp[kStreamPre];
+#pragma unroll
+  for (int j = 0; j < kStreamPre; ++j) wsp[j] = a.w_scale[(int64_t)min(j, nS - 1) * a.N + n];
+
+  // (3) the whole weight stream of this wave (the scheduling barriers keep
+  //     the loads above ahead of it in issue order)
+  __builtin_amdgcn_sched_barrier(0);
+  const int8_t *wcol = a.w + (int64_t)ntc * KT * 1024 + lane * 16;
+  v4u ring[RING];
+#pragma unroll
+  for (int d = 0; d < RING; ++d)
+    ring[d] = *reinterpret_cast<const v4u *>(wcol + (int64_t)min(d, KT - 1) * 1024);
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int i = 0; i < kStreamXR; ++i) {
+    pin_load(xr[i]);
+    if (QL == 1) pin_load(xn[QL == 1 ? i : 0]);
+    if (QL < 0) {
+      pin_load(ipv[QL < 0 ? i : 0]);
+      pin_load(inv_[QL < 0 ? i : 0]);
+    }
+  }
+  pin_load(sp_l);
+  pin_load(sn_l);
+#pragma unroll
+  for (int j = 0; j < kStreamPre; ++j) pin_load(wsp[j]);
+
+  // (4) quantise (or split) X into the two planes
+#pragma unroll
+  for (int i = 0; i < kStreamXR; ++i) {
+    const int p = tid + i * kStreamThreads;
+    if (p < a.pieces) {
+      const int row = (int)__umulhi((uint32_t)p, a.ppr_magic), c = p - row * a.pieces_per_row;
+      if (QL < 0) {
+        v2u qp, qn;
+        quant8_planes(xr[i], ipv[QL < 0 ? i : 0], inv_[QL < 0 ? i : 0], qp, qn);
+        *reinterpret_cast<v2u *>(pp + row * pitch + c * 8) = qp;
+        *reinterpret_cast<v2u *>(pn + row * pitch + c * 8) = qn;
+      } else if (QL == 0) {
+        v4u qp, qn;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t u, v;
+          split_signed(xr[i][j], u, v);
+          qp[j] = u;
+          qn[j] = v;
+        }
+        *reinterpret_cast<v4u *>(pp + row * pitch + c * 16) = qp;
+        *reinterpret_cast<v4u *>(pn + row * pitch + c * 16) = qn;
+      } else {
+        *reinterpret_cast<v4u *>(pp + row * pitch + c * 16) = xr[i];
+        *reinterpret_cast<v4u *>(pn + row * pitch + c * 16) = xn[QL == 1 ? i : 0];
+      }
+    }
+  }
+  __syncthreads();
+
+  // (5) every A fragment of the call (rows at or past M are zero)
+  const int row = lane & 15, kq = (lane >> 4) * 16;
+  const bool row_ok = row < a.M;
+  v4u fa[RING], fb[RING];
+#pragma unroll
+  for (int t = 0; t < RING; ++t) {
+    fa[t] = v4u{0u, 0u, 0u, 0u};
+    fb[t] = v4u{0u, 0u, 0u, 0u};
+  }
+  if (row_ok) {  // the other lanes' rows are zero padding: no LDS traffic for them
+    const int tmax = KT - 1;
+#pragma unroll
+    for (int t = 0; t < RING; ++t) {
+      const int tt = min(t, tmax);
+      fa[t] = *reinterpret_cast<const v4u *>(pp + row * pitch + tt * 64 + kq);
+      fb[t] = *reinterpret_cast<const v4u *>(pn + row * pitch + tt * 64 + kq);
+    }
+  }
+
+  // (6) matrix-core chain as the weight tiles arrive; fold at segment ends
+  float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto fold = [&](int seg, const v4i &P, const v4i &Q) {
+    if (DEBUG) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = (lane >> 4) * 4 + r;
+        if (active && m < a.M) {
+          const int64_t o = ((int64_t)seg * a.M + m) * a.N + n;
+          a.acc[o] = P[r];
+          a.acc[(int64_t)nS * a.M * a.N + o] = Q[r];
+        }
+      }
+    }
+    // segments fold in order: wsp[0] is this segment's scale; shift the
+    // queue and fetch the one kStreamPre segments ahead
+    const float ws = wsp[0];
+#pragma unroll
+    for (int j = 0; j + 1 < kStreamPre; ++j) wsp[j] = wsp[j + 1];
+    if (!SEG1) wsp[kStreamPre - 1] = a.w_scale[(int64_t)min(seg + kStreamPre, nS - 1) * a.N + n];
+    const float sp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sp_l), seg));
+    const float sn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sn_l), seg));
+    const float cp = sp * ws, cn = sn * ws;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      yacc[r] = __builtin_fmaf(cn, (float)Q[r], __builtin_fmaf(cp, (float)P[r], yacc[r]));
+  };
+  auto wtile = [&](int t) {
+    v4u b = ring[t];
+    if (t >= RING - 7) {  // the only slots that can lie past K
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e] = t < KT ? b[e] : 0u;
+    }
+    return b;
+  };
+  auto mfma = [](const v4u &x, const v4u &w, const v4i &c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(reinterpret_cast<const v4i &>(x),
+                                                 reinterpret_cast<const v4i &>(w), c, 0, 0, 0);
+  };
+  if (SEG1) {
+    // one K-segment: no fold until the end, so the chain is branch-free; even
+    // and odd k-tiles accumulate separately (two independent chains per
+    // half) and are added at the end (exact in int32)
+    v4i acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+    for (int t = 0; t < RING; ++t) {
+      const v4u b = wtile(t);
+      acc[(t & 1) * 2] = mfma(fa[t], b, acc[(t & 1) * 2]);
+      acc[(t & 1) * 2 + 1] = mfma(fb[t], b, acc[(t & 1) * 2 + 1]);
+    }
+    fold(0, acc[0] + acc[2], acc[1] + acc[3]);
+  } else {
+    v4i accp = {0, 0, 0, 0}, accn = {0, 0, 0, 0};
+    int seg = 0;
+#pragma unroll
+    for (int t = 0; t < RING; ++t) {
+      const v4u b = wtile(t);
+      accp = mfma(fa[t], b, accp);
+      accn = mfma(fb[t], b, accn);
+      if ((a.fold_mask >> t) & 1u) {
+        fold(seg, accp, accn);
+        accp = v4i{0, 0, 0, 0};
+        accn = v4i{0, 0, 0, 0};
+        ++seg;
+      }
+    }
+  }
+
+  // epilogue: rows (lane/16)*4 + r of column n
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = (lane >> 4) * 4 + r;
+    if (active && m < a.M) a.y[(int64_t)m * a.ld_y + n] = (uint16_t)f32_to_bf16_rne(yacc[r]);
+  }
+}
+
+template <int RING, bool SEG1>
+void launch_stream_ring(const StreamArgs &a, int ql, bool debug, dim3 grid, hipStream_t s) {
+#define SQ_STREAM(QLV, DBG) \
+  hipLaunchKernelGGL((gemm_smallm_kernel<QLV, RING, SEG1, DBG>), grid, dim3(kStreamThreads), 0, s, a)
+  if (debug) {
+    if (ql < 0) SQ_STREAM(-1, true);
+    else if (ql == 0) SQ_STREAM(0, true);
+    else SQ_STREAM(1, true);
+  } else {
+    if (ql < 0) SQ_STREAM(-1, false);
+    else if (ql == 0) SQ_STREAM(0, false);
+    else SQ_STREAM(1, false);
+  }
+#undef SQ_STREAM
+}
+
+template <int RING>
+void launch_stream_segs(const StreamArgs &a, int ql, bool debug, dim3 grid, hipStream_t s) {
+  if (a.n_kseg == 1) launch_stream_ring<RING, true>(a, ql, debug, grid, s);
+  else launch_stream_ring<RING, false>(a, ql, debug, grid, s);
+}
+
+// Shapes the streaming kernel takes; the rest go to the chunked kernel.
+bool stream_fits(const GemmProblem &p) {
+  const int64_t KT = p.K / 64;
+  const int64_t ppr = p.x ? p.K / 8 : p.K / 16;
+  return KT <= kStreamMaxKT && p.ks.n <= kStreamMaxKT && p.M * ppr <= kStreamXR * kStreamThreads;
+}
+
+hipError_t launch_stream(const GemmProblem &p, hipStream_t s) {
+  StreamArgs a{};
+  a.M = (int32_t)p.M;
+  a.N = (int32_t)p.N;
+  a.K = (int32_t)p.K;
+  const int ql = p.x ? -1 : p.q_layout;
+  a.pieces_per_row = (int32_t)(p.x ? p.K / 8 : p.K / 16);
+  a.pieces = (int32_t)(p.M * a.pieces_per_row);
+  a.ppr_magic = (uint32_t)(((1ull << 32) + a.pieces_per_row - 1) / a.pieces_per_row);
+  if (p.x) {
+    a.x = reinterpret_cast<const uint8_t *>(p.x);
+    a.ld_bytes = p.ld_x * 2;
+  } else {
+    a.x = reinterpret_cast<const uint8_t *>(p.xq);
+    a.ld_bytes = p.ld_q;
+  }
+  a.plane_stride = ql == 1 ? p.M * p.ld_q : 0;
+  a.w = p.w_packed;
+  a.w_scale = p.w_scale;
+  a.act = p.act;
+  a.y = p.y;
+  a.ld_y = p.ld_y;
+  a.acc = p.acc_debug;
+  a.n_kseg = p.ks.n;
+  a.fold_mask = 0;
+  for (int i = 0; i < p.ks.n; ++i) a.fold_mask |= 1u << (p.ks.end[i] / 64 - 1);
+  const int KT = (int)(p.K / 64);
+  const dim3 grid((unsigned)((p.N / 16 + 3) / 4));
+  const bool debug = p.acc_debug != nullptr;
+  if (KT <= 8) launch_stream_segs<8>(a, ql, debug, grid, s);
+  else if (KT <= 16) launch_stream_segs<16>(a, ql, debug, grid, s);
+  else if (KT <= 24) launch_stream_segs<24>(a, ql, debug, grid, s);
+  else launch_stream_segs<32>(a, ql, debug, grid, s);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_smallm(const GemmProblem &p, hipStream_t s) {
+  if (stream_fits(p)) return launch_stream(p, s);
   constexpr int WPG = 2;
   constexpr int NTHR = 64 * WPG;
   SmallArgs a{};
@@ -255,7 +565,7 @@ hipError_t launch_gemm_smallm(const GemmProblem &p, hipStream_t s) {
   for (int i = 0; i < p.ks.n; ++i) a.seg_end_tile[i] = p.ks.end[i] / 64;
   dim3 grid((unsigned)((p.N / 16 + WPG - 1) / WPG)), block(NTHR);
 #define SQ_SMALL(QLV, ONEV, DBG) \
-  hipLaunchKernelGGL((gemm_smallm_kernel<WPG, QLV, ONEV, DBG>), grid, block, 0, s, a)
+  hipLaunchKernelGGL((gemm_smallm_chunked_kernel<WPG, QLV, ONEV, DBG>), grid, block, 0, s, a)
 #define SQ_SMALL_Q(ONEV, DBG)              \
   do {                                     \
     if (ql < 0) SQ_SMALL(-1, ONEV, DBG);    \
@@ -263,13 +573,8 @@ hipError_t launch_gemm_smallm(const GemmProblem &p, hipStream_t s) {
     else SQ_SMALL(1, ONEV, DBG);            \
   } while (0)
   const int ql = a.q_layout;
-  const int KT = (int)(p.K / 64);
-  const bool one = KT <= kRing && KT <= a.kc_tiles;
-  if (p.acc_debug) {
-    if (one) SQ_SMALL_Q(true, true); else SQ_SMALL_Q(false, true);
-  } else {
-    if (one) SQ_SMALL_Q(true, false); else SQ_SMALL_Q(false, false);
-  }
+  if (p.acc_debug) SQ_SMALL_Q(false, true);
+  else SQ_SMALL_Q(false, false);
 #undef SQ_SMALL_Q
 #undef SQ_SMALL
   return hipGetLastError();
