@@ -183,7 +183,9 @@ int segquant_unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t 
  *              (plane 0) and A-_i (plane 1); NULL in production.
  *   flags      SEGQ_GEMM_AUTO, or force one kernel for testing.
  * Requires K % 64 == 0, N % 16 == 0, every K-segment width <=
- * SEGQ_MAX_KSEG_WIDTH, 16-byte aligned tensor pointers, ld_x and ld_q
+ * SEGQ_MAX_KSEG_WIDTH (and, with more than one K-segment, K itself <=
+ * SEGQ_MAX_KSEG_WIDTH: SEGQ_ERR_UNSUPPORTED otherwise, as the large-M kernel
+ * keeps int32 running sums over all of K), 16-byte aligned tensor pointers, ld_x and ld_q
  * multiples of 8 and 16 elements, ld_y a multiple of 2.  M may be 0 (no
  * launch).  SEGQ_GEMM_FORCE_SMALLM requires M <= 16.
  */

@@ -261,6 +261,10 @@ int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
   }
   sq::SegTable ks{};
   if ((st = read_kseg(n_kseg, kseg_offset, kseg_width, K, SEGQ_MAX_KSEG_WIDTH, ks))) return st;
+  if (ks.n > 1 && K > SEGQ_MAX_KSEG_WIDTH)
+    return fail(SEGQ_ERR_UNSUPPORTED,
+                "with several K-segments K must be <= %d (int32 running sums over all of K); K=%lld",
+                SEGQ_MAX_KSEG_WIDTH, (long long)K);
   if (M == 0) return ok();
   sq::GemmProblem p{};
   p.M = M; p.N = N; p.K = K;

@@ -11,37 +11,47 @@
 //
 // Design (CDNA4, written for gfx950 rather than after the pages' CUTLASS
 // kernel):
-//   * A workgroup of 4 waves (one per SIMD) owns a BM x BN output tile and
-//     walks K in 64-wide steps, one int8 16x16x64 matrix-core step; K-segment
-//     boundaries are multiples of 64, so a step never straddles two.
+//   * A workgroup of 4 waves (one per SIMD) owns a BM x BN output tile.  K is
+//     walked in LDS stages of 128 (two 64-wide k-steps; K-segment boundaries
+//     are multiples of 64, so a k-step never straddles two segments), one
+//     barrier per stage.  The products run on the int8 32x32x32 matrix-core
+//     instruction.
 //   * Wave w owns output columns [w*BN/4, (w+1)*BN/4) for all BM rows.  The
-//     packed weight is laid out as lane-ordered 1 KiB tiles, so each wave
-//     loads its B operands straight from memory into registers (one 16-byte
-//     load per lane per 16 columns) through a 4-step register ring: the
-//     weight never touches LDS.  Both polarity halves multiply the same B
-//     registers.
-//   * The activation tile (BM x 64) is shared by the 4 waves through LDS:
-//     every thread loads 16-byte pieces of bf16 X two steps ahead, quantises
-//     them one step ahead (the sign selects the half's inverse scale, one fp32
+//     packed weight (lane-ordered 1 KiB tiles of 64 k x 16 n) gives every
+//     lane its 16-byte piece of a 32x32x32 B operand as one load, so the
+//     weight goes from memory straight into registers, never through LDS;
+//     each operand register is refilled with the stage two ahead right after
+//     its last use.  Both polarity halves multiply the same B registers.
+//   * The activation tile (BM x 128) is shared through LDS: every thread
+//     loads 16-byte pieces of bf16 X two stages ahead, quantises them one
+//     stage ahead (the sign picks the half's inverse scale, one fp32
 //     multiply, clamp, round half to even) and writes the codes as two int8
-//     planes (X+, X-) into the other LDS stage, rows padded to 80 bytes so
-//     the operand reads are free of bank conflicts.  Pre-quantised int8
-//     input skips the arithmetic.  One barrier per step.
-//   * The quantisation VALU work of step t+1 is interleaved with the matrix
-//     core instructions of step t (sched_group_barrier), so both units run
-//     at once.
-//   * Folding K-segments (the epilogue of the pages' reconstruction):
-//       SINGLE  one K-segment: int32 accumulators over all of K, scaled once
-//               at the end: y = s_w*s+*A+ + s_w*s-*A-.
-//       STEP    every K-segment is one step (e.g. one attention head per
-//               segment): each step's products start from zero and are
-//               folded into an fp32 sum right away.
-//       MULTI   general segments: int32 accumulators per segment, folded
-//               into the fp32 sum at each segment end.
-//     The per-column weight scales are fetched ahead of their use.
+//     planes (X+, X-), rows padded to 144 bytes so that the 16-byte operand
+//     reads are free of bank conflicts.  Pre-quantised int8 input skips the
+//     arithmetic.
+//   * The stage loop is straight-line: prefetch indices are clamped instead
+//     of branched on, K is padded to whole stage pairs with zero codes, and
+//     segment look-ups are wave-uniform (scalar loads), so no vector load
+//     ever waits behind the prefetches it should overlap.
+//   * Folding K-segments (the pages' reconstruction):
+//       SINGLE  one K-segment: int32 sums over all of K, scaled once at the
+//               end: y = s_w*s+*A+ + s_w*s-*A-.
+//       STEP    every K-segment is one 64-wide k-step (one attention head per
+//               segment): each k-step's products start from zero and are
+//               folded into an fp32 sum held in registers.
+//       MULTI   general segments (MULTI64 when a segment ends inside a
+//               128-wide stage).  The int32 sums S run over all of K and are
+//               never reset; at the end of segment i the fold adds
+//               (c_i - c_{i+1}) * S_i (c_i = s_i * s_w,i per column and half,
+//               c past the last segment = 0), which telescopes to
+//               sum_i c_i * A_i.  The fp32 sum lives in LDS.  (The variant
+//               that dumps accumulators dumps the S_i; a second launch turns
+//               them into the per-segment sums.)
 //   * Workgroup -> tile order is XCD-aware: workgroups are dealt to the 8
 //     XCDs round-robin, so XCD x is given one contiguous range of row-major
 //     tiles; a block of X rows is then quantised and cached inside one L2.
+#include <stddef.h>
+
 #include <type_traits>
 
 #include "sq_device.hpp"
@@ -51,13 +61,19 @@ namespace sq {
 
 namespace {
 
-constexpr int kAPitch = 80;  // bytes per LDS row of one A plane (64 + 16 pad)
+constexpr int kAPitch = 144;  // bytes per LDS row of one A plane (128 + 16 pad)
+constexpr int kBK = 128;      // K per LDS stage
 
 enum AMode { A_BF16 = 0, A_SIGNED = 1, A_PLANES = 2 };
-enum Mode { SINGLE = 0, STEP = 1, MULTI = 2 };
+// MULTI folds at stage ends (every segment end but the last on a multiple of
+// 128); MULTI64 checks after every 64-wide k-step.
+enum Mode { SINGLE = 0, STEP = 1, MULTI = 2, MULTI64 = 3 };
 
 template <int V>
 using ic = std::integral_constant<int, V>;
+
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 struct TileArgs {
   int32_t M, N, K;
@@ -74,32 +90,48 @@ struct TileArgs {
   int64_t ld_y;
   int32_t *acc;  // [2][n_kseg][M][N] or null
   int32_t n_kseg;
-  int32_t seg_end_tile[kMaxKSeg];  // exclusive end of each segment, in 64-steps
+  int32_t seg_end_tile[kMaxKSeg];  // exclusive end of each segment, in k-tiles of 64
 };
 
-__device__ __forceinline__ v4u lds_read16(const uint8_t *p) {
-  return *reinterpret_cast<const v4u *>(p);
+// Activation pieces quantised in 32-k sub-block ks of a stage: piece i goes
+// to sub-block (3 i) / xp (none to the last one, which follows the barrier).
+constexpr int pieces_in_sub(int xp, int ks) {
+  int n = 0;
+  for (int i = 0; i < xp; ++i) n += (i * 3) / xp == ks ? 1 : 0;
+  return n;
 }
 
-__device__ __forceinline__ v4i mfma(const v4u &a, const v4u &b, const v4i &c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(reinterpret_cast<const v4i &>(a),
+// Segment end i, read straight from the kernel-argument segment (the
+// argument is the only one, at offset 0).  Indexing the by-value argument
+// itself with a run-time index would make the compiler copy all of it into
+// scratch memory first.
+__device__ __forceinline__ int seg_end_at(int i) {
+  const char *base = (const char *)__builtin_amdgcn_kernarg_segment_ptr();
+  return reinterpret_cast<const int32_t *>(base + offsetof(TileArgs, seg_end_tile))[i];
+}
+
+__device__ __forceinline__ v16i mfma32(const v4u &a, const v4u &b, const v16i &c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(reinterpret_cast<const v4i &>(a),
                                                reinterpret_cast<const v4i &>(b), c, 0, 0, 0);
 }
 
 template <int BM, int BN, int AMODE, int MODE, bool DEBUG>
-__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(TileArgs a) {
-  constexpr int WN = BN / 4, FM = BM / 16, FN = WN / 16;
+__global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) void gemm_tile_kernel(TileArgs a) {
+  constexpr int WN = BN / 4;   // columns per wave
+  constexpr int MB = BM / 32;  // 32-row blocks
+  constexpr int NB = WN / 32;  // 32-column blocks per wave
   constexpr int A_PLANE = BM * kAPitch, A_STAGE = 2 * A_PLANE;
-  // 16-byte activation pieces per thread per step
-  constexpr int XP = AMODE == A_SIGNED ? BM / 64 : BM / 32;
-  constexpr int WR = 4;  // weight register ring depth (steps)
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sizes");
+  // 16-byte activation pieces per thread per stage
+  constexpr int XP = AMODE == A_SIGNED ? BM / 32 : BM / 16;
+  static_assert(BM % 32 == 0 && WN % 32 == 0, "tile sizes");
 
-  // MULTI keeps its fp32 running sum in LDS: four floats per lane and
-  // fragment, [wave][i][j][lane][r] (16-byte accesses, conflict free)
-  constexpr int Y_LDS = MODE == MULTI ? 4 * FM * FN * 4 * 64 * 4 : 0;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * A_STAGE + Y_LDS];
-  v4f *ylds4 = reinterpret_cast<v4f *>(smem + 2 * A_STAGE);
+  // MULTI keeps its fp32 sum in LDS: [wave][mb][nb][q][lane], 4 floats each
+  constexpr int Y_LDS = (MODE == MULTI || MODE == MULTI64) ? 4 * MB * NB * 4 * 64 * 16 : 0;
+  // three stage buffers: stage u is read from buffer u % 3 while stage u + 1
+  // is written to (u + 1) % 3, so one barrier per stage suffices and it can
+  // sit before the stage's last sub-block (see the stage loop)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * A_STAGE + Y_LDS];
+  v4f *ylds = reinterpret_cast<v4f *>(smem + 3 * A_STAGE);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -114,139 +146,143 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(TileArgs a) {
   const int tm = logical / a.tiles_n, tn = logical - tm * a.tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
   const int KT = a.K / 64, NT = a.N / 16;
-  const int nt0 = n0 / 16 + wave * FN;  // first 16-column tile of this wave
+  const int KS = (KT + 1) / 2;    // stages
+  const int KSV = (KS + 1) & ~1;  // stages rounded up to pairs (padding: zero codes)
 
   const int nS = a.n_kseg;
   const float *s_pos = a.act, *s_neg = a.act + nS;
   const float *i_pos = a.act + 2 * nS, *i_neg = a.act + 3 * nS;
 
-  // ---- weight stream: B operands straight into registers ----
-  const int8_t *wbase = a.w + (int64_t)nt0 * KT * 1024 + lane * 16;
-  v4u wr[WR][FN];
-  // Loads are branch-free (indices clamped into range; the extra values are
-  // never used), so the count of loads in flight is the same on every pass
-  // and the compiler's waits stay exact: prefetching keeps working.
-  auto load_w = [&](auto SLOT, int kt) {
-    constexpr int s = decltype(SLOT)::value;
-    kt = min(kt, KT - 1);
+  // ---- weight stream: 32x32x32 B operands straight into registers ----
+  // Lane l of block nb, 32-k sub-block ks of a stage reads 16 bytes of the
+  // 1 KiB tile (n-tile nt, k-tile 2u + ks/2) at g*256 + j*16: column
+  // j = l % 16 of n-tile 2*nb + (l % 32) / 16, k group g = 2*(ks % 2) + l / 32.
+  const int lane_j = lane & 15, lane_g = lane >> 5;
+  const int nt_wave = n0 / 16 + wave * (WN / 16);
+  const int8_t *wcol[NB];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      // n-tiles past N load the last valid tile: their columns are never stored
-      const int jj = min(j, NT - 1 - nt0);
-      wr[s][j] = *reinterpret_cast<const v4u *>(wbase + ((int64_t)jj * KT + kt) * 1024);
-    }
+  for (int nb = 0; nb < NB; ++nb) {
+    // n-tiles past N read the last valid tile: those columns are never stored
+    const int nt = min(nt_wave + 2 * nb + ((lane & 31) >> 4), NT - 1);
+    wcol[nb] = a.w + (int64_t)nt * KT * 1024 + lane_j * 16 + lane_g * 256;
+  }
+  v4u wr[2][NB][4];
+  auto load_w1 = [&](auto SLOT, int nb, int ks, int u) __attribute__((always_inline)) {
+    constexpr int s = decltype(SLOT)::value;
+    const int kt = min(2 * u + (ks >> 1), KT - 1);
+    wr[s][nb][ks] = *reinterpret_cast<const v4u *>(wcol[nb] + (int64_t)kt * 1024 + (ks & 1) * 512);
   };
 
-  // ---- activation stream: 16-byte pieces, two steps ahead ----
+  // ---- activation stream: 16-byte pieces, two stages ahead ----
+  // bf16:   piece i of thread t is row i*16 + t/16, elements (t%16)*8 .. +8 of
+  //         the stage (256 bytes a row, 16 lanes a row: coalesced).
+  // signed: piece i is row i*32 + t/8, codes (t%8)*16 .. +16.
+  // planes: as signed, the first BM/32 pieces from the + plane, then the -.
+  // A thread's pieces lie in one 64-wide half of the stage (k-tile 2u or
+  // 2u+1); a half past K loads the last k-tile instead (in bounds) and
+  // stores zero codes.
+  const int my_half = AMODE == A_BF16 ? (tid & 15) >> 3 : (tid & 7) >> 2;
+  const int half_off = AMODE == A_BF16 ? (tid & 7) * 8 : (tid & 3) * 16;  // elements
   v4u xr[2][XP];
-  auto load_x = [&](auto SLOT, int kt) {
+  auto load_x = [&](auto SLOT, int u) __attribute__((always_inline)) {
     constexpr int s = decltype(SLOT)::value;
-    kt = min(kt, KT - 1);
-    {
-#pragma unroll
-      for (int i = 0; i < XP; ++i) {
-        const uint8_t *p;
-        if (AMODE == A_BF16) {
-          const int m = min(m0 + i * 32 + (tid >> 3), a.M - 1);  // rows past M: any valid row
-          p = reinterpret_cast<const uint8_t *>(a.x) + (int64_t)m * a.ld_x * 2 +
-              (int64_t)kt * 128 + (tid & 7) * 16;
-        } else if (AMODE == A_SIGNED) {
-          const int m = min(m0 + i * 64 + (tid >> 2), a.M - 1);
-          p = reinterpret_cast<const uint8_t *>(a.xq) + (int64_t)m * a.ld_q + (int64_t)kt * 64 +
-              (tid & 3) * 16;
-        } else {
-          const int half = i / (BM / 64), ii = i % (BM / 64);
-          const int m = min(m0 + ii * 64 + (tid >> 2), a.M - 1);
-          p = reinterpret_cast<const uint8_t *>(a.xq) + half * a.plane_stride +
-              (int64_t)m * a.ld_q + (int64_t)kt * 64 + (tid & 3) * 16;
-        }
-        xr[s][i] = *reinterpret_cast<const v4u *>(p);
-      }
-    }
-  };
-
-  // quantise the staged pieces of slot SLOT into LDS stage `stage`
-  auto quant_store = [&](auto SLOT, int stage, float inv_pos, float inv_neg, bool valid) {
-    constexpr int s = decltype(SLOT)::value;
-    uint8_t *ap = smem + stage * A_STAGE;
-    uint8_t *an = ap + A_PLANE;
+    const int kt = min(2 * min(u, KS - 1) + my_half, KT - 1);
+    const int64_t col = (int64_t)kt * 64 + half_off;  // element column of the piece
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
-      // a padding step past K stores zero codes (x = 0 quantises to 0)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) xr[s][i][e] = valid ? xr[s][i][e] : 0u;
+      const uint8_t *p;
       if (AMODE == A_BF16) {
-        const int off = (i * 32 + (tid >> 3)) * kAPitch + (tid & 7) * 8;
-        v2u p, n;
-        quant8_planes(xr[s][i], inv_pos, inv_neg, p, n);
-        *reinterpret_cast<v2u *>(ap + off) = p;
-        *reinterpret_cast<v2u *>(an + off) = n;
-      } else if (AMODE == A_SIGNED) {
-        const int off = (i * 64 + (tid >> 2)) * kAPitch + (tid & 3) * 16;
-        v4u p, n;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t pp, nn;
-          split_signed(xr[s][i][j], pp, nn);
-          p[j] = pp;
-          n[j] = nn;
-        }
-        *reinterpret_cast<v4u *>(ap + off) = p;
-        *reinterpret_cast<v4u *>(an + off) = n;
+        const int m = min(m0 + i * 16 + (tid >> 4), a.M - 1);  // rows past M: any valid row
+        p = reinterpret_cast<const uint8_t *>(a.x) + ((int64_t)m * a.ld_x + col) * 2;
       } else {
-        const int half = i / (BM / 64), ii = i % (BM / 64);
-        const int off = (ii * 64 + (tid >> 2)) * kAPitch + (tid & 3) * 16;
-        *reinterpret_cast<v4u *>((half ? an : ap) + off) = xr[s][i];
+        const int half = AMODE == A_PLANES ? i / (BM / 32) : 0;
+        const int ii = AMODE == A_PLANES ? i % (BM / 32) : i;
+        const int m = min(m0 + ii * 32 + (tid >> 3), a.M - 1);
+        p = reinterpret_cast<const uint8_t *>(a.xq) + half * a.plane_stride + (int64_t)m * a.ld_q + col;
       }
+      xr[s][i] = *reinterpret_cast<const v4u *>(p);
+    }
+  };
+
+  // quantise (or split) piece i of slot SLOT into the stage buffer at `buf`
+  auto quant_piece = [&](auto SLOT, int i, uint8_t *buf, float inv_pos, float inv_neg,
+                         bool valid) __attribute__((always_inline)) {
+    constexpr int s = decltype(SLOT)::value;
+    uint8_t *ap = buf;
+    uint8_t *an = buf + A_PLANE;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xr[s][i][e] = valid ? xr[s][i][e] : 0u;
+    if (AMODE == A_BF16) {
+      const int off = (i * 16 + (tid >> 4)) * kAPitch + (tid & 15) * 8;
+      v2u p, n;
+      quant8_planes(xr[s][i], inv_pos, inv_neg, p, n);
+      *reinterpret_cast<v2u *>(ap + off) = p;
+      *reinterpret_cast<v2u *>(an + off) = n;
+    } else if (AMODE == A_SIGNED) {
+      const int off = (i * 32 + (tid >> 3)) * kAPitch + (tid & 7) * 16;
+      v4u p, n;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t pp, nn;
+        split_signed(xr[s][i][j], pp, nn);
+        p[j] = pp;
+        n[j] = nn;
+      }
+      *reinterpret_cast<v4u *>(ap + off) = p;
+      *reinterpret_cast<v4u *>(an + off) = n;
+    } else {
+      const int half = i / (BM / 32), ii = i % (BM / 32);
+      const int off = (ii * 32 + (tid >> 3)) * kAPitch + (tid & 7) * 16;
+      *reinterpret_cast<v4u *>((half ? an : ap) + off) = xr[s][i];
+    }
+  };
+
+  // A-operand fragments of one 32-k sub-block, double-buffered
+  v4u fa[2][MB], fb[2][MB];
+  const int arow = (lane & 31) * kAPitch + lane_g * 16;
+  auto read_frags = [&](auto SLOT, const uint8_t *buf, int ks) __attribute__((always_inline)) {
+    constexpr int f = decltype(SLOT)::value;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      fa[f][mb] = *reinterpret_cast<const v4u *>(buf + arow + mb * 32 * kAPitch + ks * 32);
+      fb[f][mb] = *reinterpret_cast<const v4u *>(buf + A_PLANE + arow + mb * 32 * kAPitch + ks * 32);
     }
   };
 
   // ---- accumulators ----
-  constexpr bool KEEP_F32 = MODE == STEP;  // fp32 sum in registers
-  constexpr int IM = MODE == STEP ? 1 : FM, IN = MODE == STEP ? 1 : FN;
-  constexpr int YM = KEEP_F32 ? FM : 1, YN = KEEP_F32 ? FN : 1;
-  v4i accp[IM][IN], accn[IM][IN];
-  float yacc[YM][YN][4];
+  v16i accp[MB][NB], accn[MB][NB];
 #pragma unroll
-  for (int i = 0; i < IM; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < IN; ++j) {
-      accp[i][j] = v4i{0, 0, 0, 0};
-      accn[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < NB; ++j) {
+      accp[i][j] = v16i{};
+      accn[i][j] = v16i{};
     }
+  constexpr int YM = MODE == STEP ? MB : 1, YN = MODE == STEP ? NB : 1;
+  v16f yacc[YM][YN];
 #pragma unroll
   for (int i = 0; i < YM; ++i)
 #pragma unroll
-    for (int j = 0; j < YN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) yacc[i][j][r] = 0.0f;
-
-  if (MODE == MULTI) {
-    for (int e = tid; e < Y_LDS / 16; e += 256) ylds4[e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < YN; ++j) yacc[i][j] = v16f{};
+  if (MODE == MULTI || MODE == MULTI64) {
+    for (int e = tid; e < Y_LDS / 16; e += 256) ylds[e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  auto yidx4 = [&](int i, int j) { return ((wave * FM + i) * FN + j) * 64 + lane; };
-
-  const int col_lane = n0 + wave * WN + (lane & 15);  // column of fragment j: + 16*j
-  const int row_lane = m0 + (lane >> 4) * 4;          // row of fragment i, reg r: + 16*i + r
-
-  // per-column weight scales of a segment (fetched ahead of use)
-  constexpr int WSR = MODE == STEP ? WR : 1;
-  float wsr[WSR][FN];
-  auto load_ws = [&](auto SLOT, int seg) {
-    constexpr int s = decltype(SLOT)::value;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = min(col_lane + 16 * j, a.N - 1);  // past N: never stored
-      wsr[s][j] = a.w_scale[(int64_t)min(seg, nS - 1) * a.N + col];
-    }
+  auto yidx = [&](int mb, int nb, int q) __attribute__((always_inline)) {
+    return (((wave * MB + mb) * NB + nb) * 4 + q) * 64 + lane;
   };
 
-  auto dump = [&](int seg, int i, int j, const v4i &p, const v4i &n) {
-    const int col = col_lane + 16 * j;
+  // 32x32 output block: lane l holds column l % 32 and, in register r, row
+  // (r / 4) * 8 + (l / 32) * 4 + r % 4.
+  const int col_lane = n0 + wave * WN + (lane & 31);
+  const int row_lane = m0 + (lane >> 5) * 4;
+  auto out_row = [&](int mb, int r) __attribute__((always_inline)) { return row_lane + mb * 32 + (r >> 2) * 8 + (r & 3); };
+
+  auto dump = [&](int seg, int mb, int nb, const v16i &p, const v16i &n) __attribute__((always_inline)) {
+    const int col = col_lane + 32 * nb;
     if (col >= a.N) return;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = row_lane + 16 * i + r;
+    for (int r = 0; r < 16; ++r) {
+      const int m = out_row(mb, r);
       if (m >= a.M) continue;
       const int64_t o = ((int64_t)seg * a.M + m) * a.N + col;
       a.acc[o] = p[r];
@@ -254,184 +290,277 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(TileArgs a) {
     }
   };
 
-  // fold the int32 accumulators of segment `seg` into the fp32 sum
-  auto fold_multi = [&](int seg) {
-    const float sp = s_pos[seg], sn = s_neg[seg];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if (DEBUG) dump(seg, i, j, accp[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j],
-                        accn[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j]);
-        const float cp = sp * wsr[0][j], cn = sn * wsr[0][j];
-        const v4f P = __builtin_convertvector(accp[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j], v4f);
-        const v4f Q = __builtin_convertvector(accn[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j], v4f);
-        v4f &yv = ylds4[yidx4(i, j)];
-        yv = __builtin_elementwise_fma(v4f{cn, cn, cn, cn}, Q,
-                                       __builtin_elementwise_fma(v4f{cp, cp, cp, cp}, P, yv));
-        accp[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j] = v4i{0, 0, 0, 0};
-        accn[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j] = v4i{0, 0, 0, 0};
-      }
+  // weight scale of segment `seg` (clamped) for this lane's column of block nb
+  auto col_ws = [&](int seg, int nb) __attribute__((always_inline)) {
+    const int col = min(col_lane + 32 * nb, a.N - 1);  // past N: never stored
+    return a.w_scale[(int64_t)min(seg, nS - 1) * a.N + col];
   };
+
+  // ---- fold state ----
+  // STEP: the scales of the k-step being folded, fetched a stage ahead.
+  // MULTI: the column scales of the current and the next segment.
+  float wsa[NB], wsb[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    wsa[nb] = col_ws(0, nb);
+    wsb[nb] = MODE == SINGLE ? 0.0f : col_ws(1, nb);
+  }
+  // STEP: s+/s- of the k-steps being folded (even in *a, odd in *b)
+  float spa = s_pos[0], sna = s_neg[0];
+  float spb = s_pos[min(1, nS - 1)], snb = s_neg[min(1, nS - 1)];
+
+  // STEP: fold k-step t into the fp32 registers (products started from 0)
+  auto fold_step = [&](int t) __attribute__((always_inline)) {
+    const float sp = (t & 1) ? spb : spa, sn = (t & 1) ? snb : sna;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float ws = (t & 1) ? wsb[nb] : wsa[nb];
+      const float cp = sp * ws, cn = sn * ws;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if (DEBUG && t < KT) dump(t, mb, nb, accp[mb][nb], accn[mb][nb]);
+        v16f &yv = yacc[MODE == STEP ? mb : 0][MODE == STEP ? nb : 0];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)  // element by element: few temporaries
+          yv[r] = __builtin_fmaf(cn, (float)accn[mb][nb][r], __builtin_fmaf(cp, (float)accp[mb][nb][r], yv[r]));
+      }
+    }
+  };
+
+  // MULTI: fold at the end of segment seg into the LDS sum
+  auto fold_multi = [&](int seg) __attribute__((always_inline)) {
+    const float sp = s_pos[seg], sn = s_neg[seg];
+    const bool last = seg + 1 >= nS;
+    const float sp1 = last ? 0.0f : s_pos[min(seg + 1, nS - 1)];
+    const float sn1 = last ? 0.0f : s_neg[min(seg + 1, nS - 1)];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      // telescoped: S_i * (c_i - c_{i+1})
+      const float cp = sp * wsa[nb] - sp1 * wsb[nb], cn = sn * wsa[nb] - sn1 * wsb[nb];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        // (the dump holds the running sums S_i; the launcher differences them)
+        if (DEBUG) dump(seg, mb, nb, accp[mb][nb], accn[mb][nb]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // four elements at a time: few temporaries
+          const v4f Pq = {(float)accp[mb][nb][4 * q], (float)accp[mb][nb][4 * q + 1],
+                          (float)accp[mb][nb][4 * q + 2], (float)accp[mb][nb][4 * q + 3]};
+          const v4f Qq = {(float)accn[mb][nb][4 * q], (float)accn[mb][nb][4 * q + 1],
+                          (float)accn[mb][nb][4 * q + 2], (float)accn[mb][nb][4 * q + 3]};
+          v4f &yv = ylds[yidx(mb, nb, q)];
+          yv = __builtin_elementwise_fma(v4f(cn), Qq, __builtin_elementwise_fma(v4f(cp), Pq, yv));
+        }
+      }
+      wsa[nb] = wsb[nb];
+      wsb[nb] = col_ws(seg + 2, nb);
+    }
+  };
+
+  // ---- segment of each half of the stage being quantised (wave-uniform) ----
+  // k-tiles only move forward, so each index only grows; a stage advances a
+  // half by 2 k-tiles, so at most two steps per stage.
+  auto advance = [&](int &sg, int kt) __attribute__((always_inline)) {
+    sg += (kt < KT && kt >= seg_end_at(sg)) ? 1 : 0;
+    sg = min(sg, nS - 1);
+    sg += (kt < KT && kt >= seg_end_at(sg)) ? 1 : 0;
+    sg = min(sg, nS - 1);
+  };
+  int q_lo = 0, q_hi = 0;  // segments of k-tiles 2v, 2v+1 of the stage v being quantised
+  const float ip0 = i_pos[0], in0 = i_neg[0];
 
   // ---- prologue ----
-  load_w(ic<0>{}, 0);
-  load_w(ic<1>{}, 1);
-  load_w(ic<2>{}, 2);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) load_w1(ic<0>{}, nb, ks, 0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) load_w1(ic<1>{}, nb, ks, 1);
   load_x(ic<0>{}, 0);
   load_x(ic<1>{}, 1);
-  load_ws(ic<0>{}, 0);
-  if (MODE == STEP) {
-    load_ws(ic<1 % WSR>{}, 1);
-    load_ws(ic<2 % WSR>{}, 2);
+  {
+    float ip = ip0, in = in0;
+    if (MODE != SINGLE) {
+      advance(q_hi, 1);
+      const int qs = my_half ? q_hi : q_lo;
+      ip = i_pos[qs];
+      in = i_neg[qs];
+    }
+#pragma unroll
+    for (int i = 0; i < XP; ++i) quant_piece(ic<0>{}, i, smem, ip, in, my_half < KT);
   }
-  const float ip0 = i_pos[0], in0 = i_neg[0];
-  quant_store(ic<0>{}, 0, ip0, in0, true);
   __syncthreads();
+  read_frags(ic<0>{}, smem, 0);
 
-  int qseg = 0;  // segment of the step being quantised (t + 1)
-  int seg = 0;   // segment of the step being multiplied (t)
+  int seg = 0;                        // MULTI: segment of the k-step being multiplied
+  int next_end = seg_end_at(0);       // MULTI: its end, in k-tiles
 
-  // one K-step; s = t mod 4 (t0 is a multiple of 4)
-  // one K-step t = t0 + s of the loop over K rounded up to a multiple of 4;
-  // steps t >= KT multiply zero codes (padding)
-  auto step = [&](auto S, int t0) {
+  // one stage u = u0 + S (u0 even)
+  auto stage = [&](auto S, int u0) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
-    const int t = t0 + s;
-    // segment of step t+1 and its inverse scales, first (branch-free, so the
-    // whole step stays one basic block the scheduler can interleave)
-    if (MODE != SINGLE) qseg += (t + 1 < KT && t + 1 >= a.seg_end_tile[qseg]) ? 1 : 0;
-    const float q_ip = MODE == SINGLE ? ip0 : i_pos[qseg];
-    const float q_in = MODE == SINGLE ? in0 : i_neg[qseg];
-    // issue the loads of later steps first
-    load_w(ic<(s + 3) % 4>{}, t + 3);
-    load_x(ic<s % 2>{}, t + 2);
-    if (MODE == STEP) load_ws(ic<(s + 3) % WSR>{}, t + 3);
-    const uint8_t *ap = smem + (s % 2) * A_STAGE;
-    const uint8_t *an = ap + A_PLANE;
-    const int aoff = (lane & 15) * kAPitch + (lane >> 4) * 16;
-    v4u fa_p[FM], fa_n[FM];
-    if (MODE != STEP) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        fa_p[i] = lds_read16(ap + aoff + i * 16 * kAPitch);
-        fa_n[i] = lds_read16(an + aoff + i * 16 * kAPitch);
-      }
+    const int u = u0 + s;
+    // segments and inverse scales of the stage being quantised (u + 1)
+    float q_ip = ip0, q_in = in0;
+    if (MODE != SINGLE) {
+      advance(q_lo, 2 * (u + 1));
+      q_hi = max(q_hi, q_lo);
+      advance(q_hi, 2 * (u + 1) + 1);
+      q_ip = my_half ? i_pos[q_hi] : i_pos[q_lo];
+      q_in = my_half ? i_neg[q_hi] : i_neg[q_lo];
     }
-    if (MODE == STEP) {
-      const float sp = s_pos[min(t, nS - 1)], sn = s_neg[min(t, nS - 1)];
+    // activation of stage u + 2 (its slot was consumed during stage u - 1)
+    load_x(ic<s>{}, u + 2);
+    const int b_rd = u % 3;
+    const int b_wr = b_rd == 2 ? 0 : b_rd + 1;
+    const uint8_t *rd = smem + b_rd * A_STAGE;
+    uint8_t *wrb = smem + b_wr * A_STAGE;
+    const bool q_valid = 2 * (u + 1) + my_half < KT;  // halves past K store zeros
+    // Four 32-k sub-blocks.  Each issues the operand reads of the next one
+    // first, then its matrix-core work, with a share of the quantisation of
+    // stage u + 1 (into buffer b_wr) and the weight refills for stage u + 2
+    // between the matrix-core instructions.  The barrier comes before the
+    // last sub-block: by then every wave has written its share of stage
+    // u + 1, so the last sub-block can already read the first operands of
+    // stage u + 1 (and buffer b_wr was last read in stage u - 2).
+    auto sub = [&](auto KS) __attribute__((always_inline)) {
+      constexpr int ks = decltype(KS)::value;
+      if (ks == 3) {
+        __syncthreads();
+        read_frags(ic<0>{}, wrb, 0);
+      } else if (ks == 0 || ks == 2) {
+        read_frags(ic<1>{}, rd, ks + 1);
+      } else {
+        read_frags(ic<0>{}, rd, ks + 1);
+      }
+      // the reads stay ahead of this sub-block's matrix-core work, which
+      // hides their latency (left to itself the scheduler sinks them below)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const v4i zero = {0, 0, 0, 0};
-          if (j == 0) {
-            fa_p[i] = lds_read16(ap + aoff + i * 16 * kAPitch);
-            fa_n[i] = lds_read16(an + aoff + i * 16 * kAPitch);
+        for (int mb = 0; mb < MB; ++mb) {
+          const v4u &xa = (ks & 1) ? fa[1][mb] : fa[0][mb];
+          const v4u &xb = (ks & 1) ? fb[1][mb] : fb[0][mb];
+          if (MODE == STEP && (ks & 1) == 0) {  // a k-step's products start from 0
+            accp[mb][nb] = mfma32(xa, wr[s][nb][ks], v16i{});
+            accn[mb][nb] = mfma32(xb, wr[s][nb][ks], v16i{});
+          } else {
+            accp[mb][nb] = mfma32(xa, wr[s][nb][ks], accp[mb][nb]);
+            accn[mb][nb] = mfma32(xb, wr[s][nb][ks], accn[mb][nb]);
           }
-          const v4i P = mfma(fa_p[i], wr[s][j], zero);
-          const v4i Q = mfma(fa_n[i], wr[s][j], zero);
-          if (DEBUG && t < KT) dump(t, i, j, P, Q);
-          const float cp = sp * wsr[s % WSR][j], cn = sn * wsr[s % WSR][j];
+        }
+        load_w1(ic<s>{}, nb, ks, u + 2);  // refill with the stage two ahead
+      }
+      // this sub-block's share of the quantisation of stage u + 1
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float &yv = yacc[KEEP_F32 ? i : 0][KEEP_F32 ? j : 0][r];
-            yv = __builtin_fmaf(cn, (float)Q[r], __builtin_fmaf(cp, (float)P[r], yv));
+      for (int i = 0; i < XP; ++i)
+        if ((i * 3) / XP == ks) quant_piece(ic<1 - s>{}, i, wrb, q_ip, q_in, q_valid);
+      {
+        // Interleave: one matrix-core instruction, then an even share of the
+        // vector ALU work (quantisation), the weight refills spread among
+        // them, the LDS writes last.  Without it the ALU work comes in
+        // clumps of ~100 instructions during which the matrix cores idle.
+        constexpr int NMF = 2 * MB * NB;
+        constexpr int nq = pieces_in_sub(XP, ks);
+        constexpr int vpq = AMODE == A_BF16 ? 56 : AMODE == A_SIGNED ? 16 : 0;
+        constexpr int vfold = (MODE == STEP && (ks & 1)) ? MB * NB * 16 * 4 : 0;
+        constexpr int per = (nq * vpq + vfold + NMF - 1) / NMF + 1;
+#pragma unroll
+        for (int j = 0; j < NMF; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, per, 0);  // VALU
+          if (j % (NMF / NB) == NMF / NB - 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 16, 0);  // LDS writes
+      }
+      if (ks & 1) {
+        const int t = 2 * u + (ks >> 1);  // the k-step that just ended
+        if (MODE == STEP) {
+          fold_step(t);
+          // the scales of k-step t + 2, which reuses this slot
+          const int sg = min(t + 2, nS - 1);
+          if (t & 1) {
+            spb = s_pos[sg];
+            snb = s_neg[sg];
+          } else {
+            spa = s_pos[sg];
+            sna = s_neg[sg];
           }
-        }
-    } else {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          v4i &P = accp[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j];
-          v4i &Q = accn[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j];
-          P = mfma(fa_p[i], wr[s][j], P);
-          Q = mfma(fa_n[i], wr[s][j], Q);
-        }
-    }
-    // quantise step t+1 (past the end: harmless, the stage is never read)
-    quant_store(ic<(s + 1) % 2>{}, (s + 1) % 2, q_ip, q_in, t + 1 < KT);
-    // Interleave: loads, operand reads, then matrix-core instructions
-    // alternating with the VALU work (quantisation of the next step, STEP
-    // folds), LDS writes last.
-    constexpr int NMFMA = 2 * FM * FN;
-    constexpr int NQ = AMODE == A_BF16 ? 64 * XP : 12 * XP;  // quantisation VALU
-    __builtin_amdgcn_sched_group_barrier(0x020, FN + XP + (MODE == STEP ? FN : 0), 0);
-    if (MODE == STEP) {
-      // per row block: its two operand reads, then pairs of matrix-core ops
-      // each followed by the fold of the pair before and a share of the
-      // quantisation work
-      constexpr int PER = 16 + (NQ + FM * FN - 1) / (FM * FN);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+          for (int nb = 0; nb < NB; ++nb) {
+            if (t & 1) wsb[nb] = col_ws(t + 2, nb);
+            else wsa[nb] = col_ws(t + 2, nb);
+          }
+        } else if ((MODE == MULTI64 || (MODE == MULTI && ks == 3)) && t + 1 >= next_end) {
+          // (>=: at a stage end, a segment that ends with K on an odd k-tile
+          // has ended one padding k-step before)
+          fold_multi(seg);
+          ++seg;
+          next_end = seg < nS ? seg_end_at(seg) : 1 << 30;
         }
       }
-    } else {
-      constexpr int PER = (NQ + NMFMA - 1) / NMFMA;
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM, 0);
-#pragma unroll
-      for (int g = 0; g < NMFMA; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x200, 2 * XP, 0);
-    if (MODE == MULTI && seg < nS && t + 1 == a.seg_end_tile[seg]) {
-      fold_multi(seg);
-      ++seg;
-      load_ws(ic<0>{}, seg);  // the next segment's scales, needed at its end
-    }
-    __syncthreads();
+      // keep the next sub-block's operand reads and refills below this one:
+      // hoisted, they would hold two copies of the operands live at once
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    sub(ic<0>{});
+    sub(ic<1>{});
+    sub(ic<2>{});
+    sub(ic<3>{});
   };
 
-  // main loop: groups of 4 steps, straight-line (K rounded up to a multiple
-  // of 4 steps; padding steps multiply zero codes)
-  const int KTV = (KT + 3) & ~3;
-  for (int t0 = 0; t0 < KTV; t0 += 4) {
-    step(ic<0>{}, t0);
-    step(ic<1>{}, t0);
-    step(ic<2>{}, t0);
-    step(ic<3>{}, t0);
+  for (int u0 = 0; u0 < KSV; u0 += 2) {
+    stage(ic<0>{}, u0);
+    stage(ic<1>{}, u0);
   }
 
   // ---- epilogue: bf16 store ----
-  float cp[FN], cn[FN];
-  if (MODE == SINGLE) {
-    const float sp = s_pos[0], sn = s_neg[0];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      cp[j] = sp * wsr[0][j];
-      cn[j] = sn * wsr[0][j];
+  for (int nb = 0; nb < NB; ++nb) {
+    const int col = col_lane + 32 * nb;
+    float cp = 0.0f, cn = 0.0f;
+    if (MODE == SINGLE) {
+      cp = s_pos[0] * wsa[nb];
+      cn = s_neg[0] * wsa[nb];
     }
-  }
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int mb = 0; mb < MB; ++mb) {
+      if (MODE == SINGLE && DEBUG) dump(0, mb, nb, accp[mb][nb], accn[mb][nb]);
+      v16f v;
+      if (MODE == SINGLE) {
+        const v16f P = __builtin_convertvector(accp[mb][nb], v16f);
+        const v16f Q = __builtin_convertvector(accn[mb][nb], v16f);
+        v = __builtin_elementwise_fma(v16f(cn), Q, v16f(cp) * P);
+      } else if (MODE == STEP) {
+        v = yacc[MODE == STEP ? mb : 0][MODE == STEP ? nb : 0];
+      } else {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if (MODE == SINGLE && DEBUG)
-        dump(0, i, j, accp[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j],
-             accn[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j]);
-      const int col = col_lane + 16 * j;
+        for (int q = 0; q < 4; ++q) {
+          const v4f yq = ylds[yidx(mb, nb, q)];
+          v[4 * q] = yq[0];
+          v[4 * q + 1] = yq[1];
+          v[4 * q + 2] = yq[2];
+          v[4 * q + 3] = yq[3];
+        }
+      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = row_lane + 16 * i + r;
-        float v;
-        if (MODE == SINGLE)
-          v = __builtin_fmaf(cn[j], (float)accn[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j][r],
-                             cp[j] * (float)accp[MODE == STEP ? 0 : i][MODE == STEP ? 0 : j][r]);
-        else if (MODE == STEP)
-          v = yacc[KEEP_F32 ? i : 0][KEEP_F32 ? j : 0][r];
-        else
-          v = ylds4[yidx4(i, j)][r];
-        if (m < a.M && col < a.N) a.y[(int64_t)m * a.ld_y + col] = (uint16_t)f32_to_bf16_rne(v);
+      for (int r = 0; r < 16; ++r) {
+        const int m = out_row(mb, r);
+        if (m < a.M && col < a.N) a.y[(int64_t)m * a.ld_y + col] = (uint16_t)f32_to_bf16_rne(v[r]);
       }
     }
+  }
+}
+
+// The accumulator dump of a multi-segment launch holds running sums S_i;
+// turn them into per-segment sums A_i = S_i - S_{i-1} (exact in int32).
+__global__ __launch_bounds__(256) void acc_difference_kernel(int32_t *acc, int n_kseg, int64_t mn) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= 2 * mn) return;
+  const int64_t h = e / mn, o = e - h * mn;
+  int32_t *base = acc + h * n_kseg * mn + o;
+  for (int seg = n_kseg - 1; seg >= 1; --seg) base[seg * mn] -= base[(seg - 1) * mn];
 }
 
 template <int BM, int BN, int MODE>
@@ -455,7 +584,7 @@ hipError_t launch_variant(TileArgs t, int amode, bool debug, hipStream_t s) {
 }
 
 // Estimated time of a tile shape: waves of 256 workgroups (one per CU) times
-// the time of one K-step of one tile, taken as the larger of the matrix-core
+// the time of one k-step of one tile, taken as the larger of the matrix-core
 // time (BM*BN/32 cycles) and, with bf16 input, the quantisation VALU time
 // (BM*64/256 elements per thread, about 7.5 instructions of 4 cycles each).
 double tile_cost(int64_t M, int64_t N, int BM, int BN, bool bf16) {
@@ -498,8 +627,16 @@ hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s) {
       return launch_variant<64, 384, SINGLE>(t, amode, debug, s);
     return launch_variant<128, 256, SINGLE>(t, amode, debug, s);
   }
-  if (every_step) return launch_variant<64, 256, STEP>(t, amode, debug, s);
-  return launch_variant<64, 384, MULTI>(t, amode, debug, s);
+  if (every_step) return launch_variant<32, 256, STEP>(t, amode, debug, s);
+  bool even_ends = true;  // every segment end but the last on a whole stage
+  for (int i = 0; i + 1 < p.ks.n; ++i) even_ends = even_ends && (p.ks.end[i] % 128 == 0);
+  hipError_t e = even_ends ? launch_variant<64, 256, MULTI>(t, amode, debug, s)
+                           : launch_variant<64, 256, MULTI64>(t, amode, debug, s);
+  if (e != hipSuccess || !debug) return e;
+  const int64_t mn = p.M * p.N;
+  hipLaunchKernelGGL(acc_difference_kernel, dim3((unsigned)((2 * mn + 255) / 256)), dim3(256), 0, s,
+                     p.acc_debug, p.ks.n, mn);
+  return hipGetLastError();
 }
 
 }  // namespace sq

@@ -124,6 +124,7 @@ def gemm(M=64, N=64, K=128, x=FAKE, ld_x=None, xq=None, ld_q=0, q_layout=0, w=FA
     (dict(widths=[128], n_kseg=0), S.SEGQ_ERR_SEGMENTS),
     (dict(K=64 * 129, widths=[64] * 129), S.SEGQ_ERR_UNSUPPORTED),
     (dict(K=132160, widths=[132160]), S.SEGQ_ERR_UNSUPPORTED),  # int32 bound
+    (dict(K=132160, widths=[66048, 66112]), S.SEGQ_ERR_UNSUPPORTED),  # running sums over all of K
     (dict(M=17, flags=S.SEGQ_GEMM_FORCE_SMALLM), S.SEGQ_ERR_UNSUPPORTED),
     (dict(flags=3), S.SEGQ_ERR_SHAPE),
     (dict(flags=8), S.SEGQ_ERR_SHAPE),

@@ -148,9 +148,11 @@ def test_gemm_parity(case, mode):
         assert np.array_equal(acc.cpu().numpy(), ref.acc), f"int32 accumulators, flags {flags}"
         ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), ref.y)
         assert ok, f"bf16 Y out of tolerance (flags {flags}): {nbad} elements, worst excess {worst}"
-        # the production variant (no accumulator dump) gives the same Y
+        # the production variant (no accumulator dump; it may combine the
+        # segments in another fp32 order) is within the same tolerance
         y2, _ = gpu.run(mode, flags=flags, debug=False)
-        assert torch.equal(y2, y)
+        ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y2), ref.y)
+        assert ok, f"production Y out of tolerance (flags {flags}): {nbad} elements, worst {worst}"
 
 
 def test_gemm_empty_batch_is_a_noop():
@@ -204,4 +206,5 @@ def test_full_size_workload(name):
     ridx = torch.from_numpy(rows).to(DEV)
     acc_rows = acc.index_select(2, ridx).cpu().numpy()
     assert np.array_equal(acc_rows, ref.acc), f"{name}: int32 accumulators differ"
-    assert torch.equal(yd, y)
+    ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(yd)[rows], ref.y, ymax)
+    assert ok, f"{name}: accumulator-dumping variant out of tolerance, worst excess {worst}"
