@@ -48,8 +48,9 @@
 //               that dumps accumulators dumps the S_i; a second launch turns
 //               them into the per-segment sums.)
 //   * Workgroup -> tile order is XCD-aware: workgroups are dealt to the 8
-//     XCDs round-robin, so XCD x is given one contiguous range of row-major
-//     tiles; a block of X rows is then quantised and cached inside one L2.
+//     XCDs round-robin, so XCD x is given one contiguous range of logical
+//     tiles, ordered in groups of 8 row tiles so that the tiles an XCD runs
+//     at once share weight and activation slices in its L2.
 #include <stddef.h>
 
 #include <type_traits>
@@ -143,7 +144,20 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
     const int bid = blockIdx.x, per = T / 8, rem = T % 8, x = bid % 8, i = bid / 8;
     logical = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + i;
   }
-  const int tm = logical / a.tiles_n, tn = logical - tm * a.tiles_n;
+  // Logical order: groups of up to 8 row tiles, within a group the row
+  // tile fastest.  The 32 workgroups an XCD runs at once then cover about 8
+  // row tiles x 4 column tiles, so each weight slice is read by 8 of them
+  // and each activation slice by 4 while it is in that XCD's L2.
+  int tm, tn;
+  {
+    const int GM = min(8, a.tiles_m);
+    const int group = logical / (GM * a.tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(a.tiles_m - first_m, GM);
+    const int in = logical - group * GM * a.tiles_n;
+    tm = first_m + in % gm;
+    tn = in / gm;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int KT = a.K / 64, NT = a.N / 16;
   const int KS = (KT + 1) / 2;    // stages
@@ -359,11 +373,15 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
   // ---- segment of each half of the stage being quantised (wave-uniform) ----
   // k-tiles only move forward, so each index only grows; a stage advances a
   // half by 2 k-tiles, so at most two steps per stage.
+  // Branch-free on purpose: as branches, the compiler carried the condition
+  // through a vector register that an in-flight load targets, and waited for
+  // every outstanding prefetch (vmcnt(0)) twice a stage.
   auto advance = [&](int &sg, int kt) __attribute__((always_inline)) {
-    sg += (kt < KT && kt >= seg_end_at(sg)) ? 1 : 0;
-    sg = min(sg, nS - 1);
-    sg += (kt < KT && kt >= seg_end_at(sg)) ? 1 : 0;
-    sg = min(sg, nS - 1);
+    const int in_k = kt < KT ? 1 : 0;
+    const int e1 = seg_end_at(sg);  // sg < nS throughout
+    sg = min(sg + (in_k & (kt >= e1 ? 1 : 0)), nS - 1);
+    const int e2 = seg_end_at(sg);
+    sg = min(sg + (in_k & (kt >= e2 ? 1 : 0)), nS - 1);
   };
   int q_lo = 0, q_hi = 0;  // segments of k-tiles 2v, 2v+1 of the stage v being quantised
   const float ip0 = i_pos[0], in0 = i_neg[0];
