@@ -23,16 +23,19 @@
 //     each operand register is refilled with the stage two ahead right after
 //     its last use.  Both polarity halves multiply the same B registers.
 //   * The activation tile (BM x 128) is shared through LDS: every thread
-//     loads 16-byte pieces of bf16 X two stages ahead, quantises them one
-//     stage ahead (the sign picks the half's inverse scale, one fp32
-//     multiply, clamp, round half to even) and writes the codes as two int8
-//     planes (X+, X-), rows padded to 144 bytes so that the 16-byte operand
-//     reads are free of bank conflicts.  Pre-quantised int8 input skips the
+//     loads 16-byte pieces of bf16 X into register slots (three stages
+//     ahead with one K-segment, two when segments are folded and the
+//     registers are needed for the fp32 sums), quantises them one stage
+//     ahead (the sign picks the half's inverse scale, one fp32 multiply,
+//     clamp, round half to even) and writes the codes as two int8 planes
+//     (X+, X-), rows padded to 144 bytes so that the 16-byte operand reads
+//     are free of bank conflicts.  Pre-quantised int8 input skips the
 //     arithmetic.
 //   * The stage loop is straight-line: prefetch indices are clamped instead
 //     of branched on, K is padded to whole stage pairs with zero codes, and
-//     segment look-ups are wave-uniform (scalar loads), so no vector load
-//     ever waits behind the prefetches it should overlap.
+//     per-segment values (ends, scales, inverse scales) are read from tables
+//     spread across the lanes with wave-uniform indices, so no vector load
+//     or LDS access ever waits behind the prefetches it should overlap.
 //   * Folding K-segments (the pages' reconstruction):
 //       SINGLE  one K-segment: int32 sums over all of K, scaled once at the
 //               end: y = s_w*s+*A+ + s_w*s-*A-.
@@ -44,7 +47,7 @@
 //               never reset; at the end of segment i the fold adds
 //               (c_i - c_{i+1}) * S_i (c_i = s_i * s_w,i per column and half,
 //               c past the last segment = 0), which telescopes to
-//               sum_i c_i * A_i.  The fp32 sum lives in LDS.  (The variant
+//               sum_i c_i * A_i.  The fp32 sum lives in registers.  (The variant
 //               that dumps accumulators dumps the S_i; a second launch turns
 //               them into the per-segment sums.)
 //   * Workgroup -> tile order is XCD-aware: workgroups are dealt to the 8
@@ -126,13 +129,11 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
   constexpr int XP = AMODE == A_SIGNED ? BM / 32 : BM / 16;
   static_assert(BM % 32 == 0 && WN % 32 == 0, "tile sizes");
 
-  // MULTI keeps its fp32 sum in LDS: [wave][mb][nb][q][lane], 4 floats each
-  constexpr int Y_LDS = (MODE == MULTI || MODE == MULTI64) ? 4 * MB * NB * 4 * 64 * 16 : 0;
-  // three stage buffers: stage u is read from buffer u % 3 while stage u + 1
-  // is written to (u + 1) % 3, so one barrier per stage suffices and it can
-  // sit before the stage's last sub-block (see the stage loop)
-  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * A_STAGE + Y_LDS];
-  v4f *ylds = reinterpret_cast<v4f *>(smem + 3 * A_STAGE);
+  // three stage buffers of quantised planes: stage u is read from buffer
+  // u % 3 while stage u + 1 is written to (u + 1) % 3, so one barrier per
+  // stage suffices and it can sit before the stage's last sub-block
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * A_STAGE];
+
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
     wr[s][nb][ks] = *reinterpret_cast<const v4u *>(wcol[nb] + (int64_t)kt * 1024 + (ks & 1) * 512);
   };
 
-  // ---- activation stream: 16-byte pieces, two stages ahead ----
+  // ---- activation stream: 16-byte pieces, three stages ahead ----
   // bf16:   piece i of thread t is row i*16 + t/16, elements (t%16)*8 .. +8 of
   //         the stage (256 bytes a row, 16 lanes a row: coalesced).
   // signed: piece i is row i*32 + t/8, codes (t%8)*16 .. +16.
@@ -197,7 +198,12 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
   // stores zero codes.
   const int my_half = AMODE == A_BF16 ? (tid & 15) >> 3 : (tid & 7) >> 2;
   const int half_off = AMODE == A_BF16 ? (tid & 7) * 8 : (tid & 3) * 16;  // elements
-  v4u xr[2][XP];
+  // XS register slots: stage v's pieces go to slot v % XS, loaded at the
+  // start of stage v - XS and quantised during stage v - 1 (XS - 1 stages of
+  // memory latency hidden).  Three for the single-segment loop; the fold
+  // modes need the registers and keep two.
+  constexpr int XS = MODE == SINGLE ? 3 : 2;
+  v4u xr[XS][XP];
   auto load_x = [&](auto SLOT, int u) __attribute__((always_inline)) {
     constexpr int s = decltype(SLOT)::value;
     const int kt = min(2 * min(u, KS - 1) + my_half, KT - 1);
@@ -218,18 +224,19 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
     }
   };
 
-  // quantise (or split) piece i of slot SLOT into the stage buffer at `buf`
+  // quantise (or split) piece i of X slot SLOT into the stage buffer at `buf`
   auto quant_piece = [&](auto SLOT, int i, uint8_t *buf, float inv_pos, float inv_neg,
                          bool valid) __attribute__((always_inline)) {
     constexpr int s = decltype(SLOT)::value;
     uint8_t *ap = buf;
     uint8_t *an = buf + A_PLANE;
+    v4u xv = xr[s][i];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) xr[s][i][e] = valid ? xr[s][i][e] : 0u;
+    for (int e = 0; e < 4; ++e) xv[e] = valid ? xv[e] : 0u;
     if (AMODE == A_BF16) {
       const int off = (i * 16 + (tid >> 4)) * kAPitch + (tid & 15) * 8;
       v2u p, n;
-      quant8_planes(xr[s][i], inv_pos, inv_neg, p, n);
+      quant8_planes(xv, inv_pos, inv_neg, p, n);
       *reinterpret_cast<v2u *>(ap + off) = p;
       *reinterpret_cast<v2u *>(an + off) = n;
     } else if (AMODE == A_SIGNED) {
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t pp, nn;
-        split_signed(xr[s][i][j], pp, nn);
+        split_signed(xv[j], pp, nn);
         p[j] = pp;
         n[j] = nn;
       }
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
     } else {
       const int half = i / (BM / 32), ii = i % (BM / 32);
       const int off = (ii * 32 + (tid >> 3)) * kAPitch + (tid & 7) * 16;
-      *reinterpret_cast<v4u *>((half ? an : ap) + off) = xr[s][i];
+      *reinterpret_cast<v4u *>((half ? an : ap) + off) = xv;
     }
   };
 
@@ -272,18 +279,13 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
       accp[i][j] = v16i{};
       accn[i][j] = v16i{};
     }
-  constexpr int YM = MODE == STEP ? MB : 1, YN = MODE == STEP ? NB : 1;
+  constexpr bool YREG = MODE != SINGLE;  // fp32 sums of the segment folds
+  constexpr int YM = YREG ? MB : 1, YN = YREG ? NB : 1;
   v16f yacc[YM][YN];
 #pragma unroll
   for (int i = 0; i < YM; ++i)
 #pragma unroll
     for (int j = 0; j < YN; ++j) yacc[i][j] = v16f{};
-  if (MODE == MULTI || MODE == MULTI64) {
-    for (int e = tid; e < Y_LDS / 16; e += 256) ylds[e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  auto yidx = [&](int mb, int nb, int q) __attribute__((always_inline)) {
-    return (((wave * MB + mb) * NB + nb) * 4 + q) * 64 + lane;
-  };
 
   // 32x32 output block: lane l holds column l % 32 and, in register r, row
   // (r / 4) * 8 + (l / 32) * 4 + r % 4.
@@ -310,6 +312,33 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
     return a.w_scale[(int64_t)min(seg, nS - 1) * a.N + col];
   };
 
+  // ---- per-segment tables, held across lanes ----
+  // Lane l of entry j holds segment 64 j + l (clamped).  Looked up with
+  // readlane, so the index must be wave-uniform; no scalar-memory loads in
+  // the stage loop, whose results would need a wait for every outstanding
+  // LDS access.
+  int t_end[2];
+  float t_sp[2], t_sn[2], t_ip[2], t_in[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sg = min(64 * j + lane, nS - 1);
+    t_end[j] = seg_end_at(sg);
+    t_sp[j] = s_pos[sg];
+    t_sn[j] = s_neg[sg];
+    t_ip[j] = i_pos[sg];
+    t_in[j] = i_neg[sg];
+  }
+  auto seg_i = [&](const int (&t)[2], int idx) __attribute__((always_inline)) {
+    const int lo = __builtin_amdgcn_readlane(t[0], idx & 63);
+    const int hi = __builtin_amdgcn_readlane(t[1], idx & 63);
+    return idx < 64 ? lo : hi;
+  };
+  auto seg_f = [&](const float (&t)[2], int idx) __attribute__((always_inline)) {
+    const int lo = __builtin_amdgcn_readlane(__float_as_int(t[0]), idx & 63);
+    const int hi = __builtin_amdgcn_readlane(__float_as_int(t[1]), idx & 63);
+    return __int_as_float(idx < 64 ? lo : hi);
+  };
+
   // ---- fold state ----
   // STEP: the scales of the k-step being folded, fetched a stage ahead.
   // MULTI: the column scales of the current and the next segment.
@@ -320,8 +349,8 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
     wsb[nb] = MODE == SINGLE ? 0.0f : col_ws(1, nb);
   }
   // STEP: s+/s- of the k-steps being folded (even in *a, odd in *b)
-  float spa = s_pos[0], sna = s_neg[0];
-  float spb = s_pos[min(1, nS - 1)], snb = s_neg[min(1, nS - 1)];
+  float spa = seg_f(t_sp, 0), sna = seg_f(t_sn, 0);
+  float spb = seg_f(t_sp, min(1, nS - 1)), snb = seg_f(t_sn, min(1, nS - 1));
 
   // STEP: fold k-step t into the fp32 registers (products started from 0)
   auto fold_step = [&](int t) __attribute__((always_inline)) {
@@ -333,7 +362,7 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         if (DEBUG && t < KT) dump(t, mb, nb, accp[mb][nb], accn[mb][nb]);
-        v16f &yv = yacc[MODE == STEP ? mb : 0][MODE == STEP ? nb : 0];
+        v16f &yv = yacc[YREG ? mb : 0][YREG ? nb : 0];
 #pragma unroll
         for (int r = 0; r < 16; ++r)  // element by element: few temporaries
           yv[r] = __builtin_fmaf(cn, (float)accn[mb][nb][r], __builtin_fmaf(cp, (float)accp[mb][nb][r], yv[r]));
@@ -341,12 +370,12 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
     }
   };
 
-  // MULTI: fold at the end of segment seg into the LDS sum
+  // MULTI: fold at the end of segment seg into the fp32 registers
   auto fold_multi = [&](int seg) __attribute__((always_inline)) {
-    const float sp = s_pos[seg], sn = s_neg[seg];
+    const float sp = seg_f(t_sp, seg), sn = seg_f(t_sn, seg);
     const bool last = seg + 1 >= nS;
-    const float sp1 = last ? 0.0f : s_pos[min(seg + 1, nS - 1)];
-    const float sn1 = last ? 0.0f : s_neg[min(seg + 1, nS - 1)];
+    const float sp1 = last ? 0.0f : seg_f(t_sp, min(seg + 1, nS - 1));
+    const float sn1 = last ? 0.0f : seg_f(t_sn, min(seg + 1, nS - 1));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       // telescoped: S_i * (c_i - c_{i+1})
@@ -355,15 +384,10 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
       for (int mb = 0; mb < MB; ++mb) {
         // (the dump holds the running sums S_i; the launcher differences them)
         if (DEBUG) dump(seg, mb, nb, accp[mb][nb], accn[mb][nb]);
+        v16f &yv = yacc[YREG ? mb : 0][YREG ? nb : 0];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {  // four elements at a time: few temporaries
-          const v4f Pq = {(float)accp[mb][nb][4 * q], (float)accp[mb][nb][4 * q + 1],
-                          (float)accp[mb][nb][4 * q + 2], (float)accp[mb][nb][4 * q + 3]};
-          const v4f Qq = {(float)accn[mb][nb][4 * q], (float)accn[mb][nb][4 * q + 1],
-                          (float)accn[mb][nb][4 * q + 2], (float)accn[mb][nb][4 * q + 3]};
-          v4f &yv = ylds[yidx(mb, nb, q)];
-          yv = __builtin_elementwise_fma(v4f(cn), Qq, __builtin_elementwise_fma(v4f(cp), Pq, yv));
-        }
+        for (int r = 0; r < 16; ++r)
+          yv[r] = __builtin_fmaf(cn, (float)accn[mb][nb][r], __builtin_fmaf(cp, (float)accp[mb][nb][r], yv[r]));
       }
       wsa[nb] = wsb[nb];
       wsb[nb] = col_ws(seg + 2, nb);
@@ -378,15 +402,21 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
   // every outstanding prefetch (vmcnt(0)) twice a stage.
   auto advance = [&](int &sg, int kt) __attribute__((always_inline)) {
     const int in_k = kt < KT ? 1 : 0;
-    const int e1 = seg_end_at(sg);  // sg < nS throughout
+    const int e1 = seg_i(t_end, sg);  // sg < nS throughout
     sg = min(sg + (in_k & (kt >= e1 ? 1 : 0)), nS - 1);
-    const int e2 = seg_end_at(sg);
+    const int e2 = seg_i(t_end, sg);
     sg = min(sg + (in_k & (kt >= e2 ? 1 : 0)), nS - 1);
   };
   int q_lo = 0, q_hi = 0;  // segments of k-tiles 2v, 2v+1 of the stage v being quantised
   const float ip0 = i_pos[0], in0 = i_neg[0];
 
   // ---- prologue ----
+  // (activation first, then weights: the loop's waits are computed from the
+  // order of loads on entry as well as in steady state, and this order keeps
+  // the two alike, so no wait in the loop is stricter than it needs to be)
+  load_x(ic<0>{}, 0);
+  load_x(ic<1>{}, 1);
+  if (XS == 3) load_x(ic<XS == 3 ? 2 : 0>{}, 2);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -395,15 +425,16 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) load_w1(ic<1>{}, nb, ks, 1);
-  load_x(ic<0>{}, 0);
-  load_x(ic<1>{}, 1);
   {
     float ip = ip0, in = in0;
     if (MODE != SINGLE) {
       advance(q_hi, 1);
-      const int qs = my_half ? q_hi : q_lo;
-      ip = i_pos[qs];
-      in = i_neg[qs];
+      // (the table look-up needs a wave-uniform index: read both halves'
+      // scales, then pick per lane)
+      const float ip_lo = seg_f(t_ip, q_lo), ip_hi = seg_f(t_ip, q_hi);
+      const float in_lo = seg_f(t_in, q_lo), in_hi = seg_f(t_in, q_hi);
+      ip = my_half ? ip_hi : ip_lo;
+      in = my_half ? in_hi : in_lo;
     }
 #pragma unroll
     for (int i = 0; i < XP; ++i) quant_piece(ic<0>{}, i, smem, ip, in, my_half < KT);
@@ -412,23 +443,27 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
   read_frags(ic<0>{}, smem, 0);
 
   int seg = 0;                        // MULTI: segment of the k-step being multiplied
-  int next_end = seg_end_at(0);       // MULTI: its end, in k-tiles
+  int next_end = seg_i(t_end, 0);     // MULTI: its end, in k-tiles
 
-  // one stage u = u0 + S (u0 even)
-  auto stage = [&](auto S, int u0) __attribute__((always_inline)) {
+  // one stage u; S = u % 2 (weight slots), S3 = u % 3 (activation slots)
+  auto stage = [&](auto S, auto S3, int u) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
-    const int u = u0 + s;
+    constexpr int s3 = decltype(S3)::value;
     // segments and inverse scales of the stage being quantised (u + 1)
     float q_ip = ip0, q_in = in0;
     if (MODE != SINGLE) {
       advance(q_lo, 2 * (u + 1));
       q_hi = max(q_hi, q_lo);
       advance(q_hi, 2 * (u + 1) + 1);
-      q_ip = my_half ? i_pos[q_hi] : i_pos[q_lo];
-      q_in = my_half ? i_neg[q_hi] : i_neg[q_lo];
+      const float ip_lo = seg_f(t_ip, q_lo), ip_hi = seg_f(t_ip, q_hi);
+      const float in_lo = seg_f(t_in, q_lo), in_hi = seg_f(t_in, q_hi);
+      q_ip = my_half ? ip_hi : ip_lo;
+      q_in = my_half ? in_hi : in_lo;
     }
-    // activation of stage u + 2 (its slot was consumed during stage u - 1)
-    load_x(ic<s>{}, u + 2);
+    // activation of stage u + XS (into slot u % XS, whose stage u was
+    // quantised during stage u - 1)
+    constexpr int x_load = XS == 3 ? s3 : s, x_quant = XS == 3 ? (s3 + 1) % 3 : 1 - s;
+    load_x(ic<x_load>{}, u + XS);
     const int b_rd = u % 3;
     const int b_wr = b_rd == 2 ? 0 : b_rd + 1;
     const uint8_t *rd = smem + b_rd * A_STAGE;
@@ -473,7 +508,7 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
       // this sub-block's share of the quantisation of stage u + 1
 #pragma unroll
       for (int i = 0; i < XP; ++i)
-        if ((i * 3) / XP == ks) quant_piece(ic<1 - s>{}, i, wrb, q_ip, q_in, q_valid);
+        if ((i * 3) / XP == ks) quant_piece(ic<x_quant>{}, i, wrb, q_ip, q_in, q_valid);
       {
         // Interleave: one matrix-core instruction, then an even share of the
         // vector ALU work (quantisation), the weight refills spread among
@@ -499,11 +534,11 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
           // the scales of k-step t + 2, which reuses this slot
           const int sg = min(t + 2, nS - 1);
           if (t & 1) {
-            spb = s_pos[sg];
-            snb = s_neg[sg];
+            spb = seg_f(t_sp, sg);
+            snb = seg_f(t_sn, sg);
           } else {
-            spa = s_pos[sg];
-            sna = s_neg[sg];
+            spa = seg_f(t_sp, sg);
+            sna = seg_f(t_sn, sg);
           }
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
@@ -515,7 +550,7 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
           // has ended one padding k-step before)
           fold_multi(seg);
           ++seg;
-          next_end = seg < nS ? seg_end_at(seg) : 1 << 30;
+          next_end = seg < nS ? seg_i(t_end, seg) : 1 << 30;
         }
       }
       // keep the next sub-block's operand reads and refills below this one:
@@ -528,9 +563,30 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
     sub(ic<3>{});
   };
 
-  for (int u0 = 0; u0 < KSV; u0 += 2) {
-    stage(ic<0>{}, u0);
-    stage(ic<1>{}, u0);
+  // six stages per iteration when the activation slots repeat every 3 (the
+  // weight slots every 2), then the remaining 0, 2 or 4 stages
+  int u0 = 0;
+  if (XS == 2) {
+    for (; u0 < KSV; u0 += 2) {
+      stage(ic<0>{}, ic<0>{}, u0);
+      stage(ic<1>{}, ic<0>{}, u0 + 1);
+    }
+  }
+  for (; u0 + 6 <= KSV; u0 += 6) {
+    stage(ic<0>{}, ic<0>{}, u0);
+    stage(ic<1>{}, ic<1>{}, u0 + 1);
+    stage(ic<0>{}, ic<2>{}, u0 + 2);
+    stage(ic<1>{}, ic<0>{}, u0 + 3);
+    stage(ic<0>{}, ic<1>{}, u0 + 4);
+    stage(ic<1>{}, ic<2>{}, u0 + 5);
+  }
+  if (u0 + 2 <= KSV) {
+    stage(ic<0>{}, ic<0>{}, u0);
+    stage(ic<1>{}, ic<1>{}, u0 + 1);
+  }
+  if (u0 + 4 <= KSV) {
+    stage(ic<0>{}, ic<2>{}, u0 + 2);
+    stage(ic<1>{}, ic<0>{}, u0 + 3);
   }
 
   // ---- epilogue: bf16 store ----
@@ -550,17 +606,8 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
         const v16f P = __builtin_convertvector(accp[mb][nb], v16f);
         const v16f Q = __builtin_convertvector(accn[mb][nb], v16f);
         v = __builtin_elementwise_fma(v16f(cn), Q, v16f(cp) * P);
-      } else if (MODE == STEP) {
-        v = yacc[MODE == STEP ? mb : 0][MODE == STEP ? nb : 0];
       } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v4f yq = ylds[yidx(mb, nb, q)];
-          v[4 * q] = yq[0];
-          v[4 * q + 1] = yq[1];
-          v[4 * q + 2] = yq[2];
-          v[4 * q + 3] = yq[3];
-        }
+        v = yacc[YREG ? mb : 0][YREG ? nb : 0];
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -601,18 +648,6 @@ hipError_t launch_variant(TileArgs t, int amode, bool debug, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Estimated time of a tile shape: waves of 256 workgroups (one per CU) times
-// the time of one k-step of one tile, taken as the larger of the matrix-core
-// time (BM*BN/32 cycles) and, with bf16 input, the quantisation VALU time
-// (BM*64/256 elements per thread, about 7.5 instructions of 4 cycles each).
-double tile_cost(int64_t M, int64_t N, int BM, int BN, bool bf16) {
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int64_t waves = (tiles + 255) / 256;
-  const double mfma = (double)BM * BN / 32.0;
-  const double valu = bf16 ? (double)BM * 64 / 256.0 * 7.5 * 4.0 : 0.0;
-  return (double)waves * (mfma > valu ? mfma : valu);
-}
-
 }  // namespace
 
 hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s) {
@@ -639,12 +674,7 @@ hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s) {
   }
   const int amode = p.x ? A_BF16 : (p.q_layout == 1 ? A_PLANES : A_SIGNED);
   const bool debug = p.acc_debug != nullptr;
-  const bool bf16 = amode == A_BF16;
-  if (p.ks.n == 1) {
-    if (tile_cost(p.M, p.N, 64, 384, bf16) <= tile_cost(p.M, p.N, 128, 256, bf16))
-      return launch_variant<64, 384, SINGLE>(t, amode, debug, s);
-    return launch_variant<128, 256, SINGLE>(t, amode, debug, s);
-  }
+  if (p.ks.n == 1) return launch_variant<64, 384, SINGLE>(t, amode, debug, s);
   if (every_step) return launch_variant<32, 256, STEP>(t, amode, debug, s);
   bool even_ends = true;  // every segment end but the last on a whole stage
   for (int i = 0; i + 1 < p.ks.n; ++i) even_ends = even_ends && (p.ks.end[i] % 128 == 0);
