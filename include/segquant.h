@@ -85,6 +85,8 @@ extern "C" {
 #define SEGQ_GEMM_AUTO 0u        /* pick the kernel from the shape */
 #define SEGQ_GEMM_FORCE_TILE 1u  /* the MFMA tile kernel, any M */
 #define SEGQ_GEMM_FORCE_SMALLM 2u /* the weight-streaming kernel (M <= 16) */
+#define SEGQ_GEMM_FUSED_QUANT 4u  /* quantise bf16 input inside the GEMM kernel
+                                     even when a workspace is given */
 
 /* Kernel choices reported by segquant_gemm_kernel_for. */
 #define SEGQ_KERNEL_TILE 1
@@ -181,7 +183,17 @@ int segquant_unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t 
  *   acc_debug  optional device int32 [2][n_kseg][M][N]: when not NULL the
  *              kernel also stores every per-segment accumulator A+_i
  *              (plane 0) and A-_i (plane 1); NULL in production.
- *   flags      SEGQ_GEMM_AUTO, or force one kernel for testing.
+ *   workspace  optional device scratch of workspace_bytes bytes, 16-byte
+ *              aligned, owned by the caller.  With bf16 input and at least
+ *              segquant_gemm_workspace_bytes() bytes, the call may quantise
+ *              X into it first (the segquant_quantize_dualscale kernel,
+ *              signed codes, ld_q = K) and run the GEMM from the codes: two
+ *              launches, the same results.  Its contents are undefined
+ *              afterwards; calls that share one workspace must be ordered
+ *              (same stream).  NULL, or fewer bytes than asked for: one
+ *              fused launch.
+ *   flags      SEGQ_GEMM_AUTO, or force one kernel for testing
+ *              (SEGQ_GEMM_FUSED_QUANT: never use the workspace).
  * Requires K % 64 == 0, N % 16 == 0, every K-segment width <=
  * SEGQ_MAX_KSEG_WIDTH (and, with more than one K-segment, K itself <=
  * SEGQ_MAX_KSEG_WIDTH: SEGQ_ERR_UNSUPPORTED otherwise, as the large-M kernel
@@ -196,7 +208,21 @@ int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
                            int32_t n_kseg, const int32_t *kseg_offset,
                            const int32_t *kseg_width, const float *act_scales,
                            uint16_t *y_bf16, int64_t ld_y, int32_t *acc_debug,
+                           void *workspace, size_t workspace_bytes,
                            uint32_t flags, void *stream);
+
+/*
+ * segquant_gemm_workspace_bytes -- the workspace with which
+ * segquant_gemm_w8a8_seg, given bf16 input of this shape and these
+ * K-segments, quantises first (M * K bytes), or 0 when it quantises inside
+ * the GEMM kernel anyway.  The large-M kernel re-quantises each activation
+ * tile once per output column tile; from six column tiles on, one separate
+ * quantisation pass costs less.  On invalid arguments returns 0 and sets
+ * segquant_last_error().
+ */
+size_t segquant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t n_kseg,
+                                     const int32_t *kseg_offset, const int32_t *kseg_width,
+                                     uint32_t flags);
 
 /* Which kernel segquant_gemm_w8a8_seg runs for this shape under `flags`
  * (SEGQ_KERNEL_*), or a negative status when the shape is invalid. */

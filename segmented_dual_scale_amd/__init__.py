@@ -29,7 +29,7 @@ __all__ = [
     "segquant_quantize_weight", "segquant_unpack_weight", "segquant_gemm_w8a8_seg",
     "segquant_gemm_kernel_for", "segquant_status_string", "segquant_last_error",
     "segquant_version", "SEGQ_Q_SIGNED", "SEGQ_Q_PLANES", "SEGQ_GEMM_AUTO",
-    "SEGQ_GEMM_FORCE_TILE", "SEGQ_GEMM_FORCE_SMALLM", "SEGQ_KERNEL_TILE", "SEGQ_KERNEL_SMALLM",
+    "SEGQ_GEMM_FORCE_TILE", "SEGQ_GEMM_FORCE_SMALLM", "SEGQ_GEMM_FUSED_QUANT", "SEGQ_KERNEL_TILE", "SEGQ_KERNEL_SMALLM",
 ]
 
 SEGQ_OK = 0
@@ -46,6 +46,7 @@ SEGQ_Q_PLANES = 1
 SEGQ_GEMM_AUTO = 0
 SEGQ_GEMM_FORCE_TILE = 1
 SEGQ_GEMM_FORCE_SMALLM = 2
+SEGQ_GEMM_FUSED_QUANT = 4
 SEGQ_KERNEL_TILE = 1
 SEGQ_KERNEL_SMALLM = 2
 
@@ -80,7 +81,8 @@ def load_library():
         "segquant_quantize_weight": [P, I64, I64, I64, I32, P, P, I32, P, P, I32, P, P, P],
         "segquant_unpack_weight": [P, I64, I64, P, I64, P],
         "segquant_gemm_w8a8_seg": [I64, I64, I64, P, I64, P, I64, I32, P, P, I32, P, P, P, P, I64,
-                                   P, U32, P],
+                                   P, P, ctypes.c_size_t, U32, P],
+        "segquant_gemm_workspace_bytes": [I64, I64, I64, I32, P, P, U32],
         "segquant_gemm_kernel_for": [I64, I64, I64, U32],
         "segquant_version": [],
         "segquant_status_string": [ctypes.c_int],
@@ -94,6 +96,7 @@ def load_library():
     lib.segquant_status_string.restype = ctypes.c_char_p
     lib.segquant_last_error.restype = ctypes.c_char_p
     lib.segquant_weight_packed_bytes.restype = ctypes.c_size_t
+    lib.segquant_gemm_workspace_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -223,16 +226,28 @@ def segquant_unpack_weight(w_packed, K: int, N: int, out=None):
     return out
 
 
+def segquant_gemm_workspace_bytes(M: int, N: int, K: int, kseg: Optional[Sequence[int]] = None,
+                                  flags: int = SEGQ_GEMM_AUTO) -> int:
+    off, wid = _segs(kseg, K)
+    return int(load_library().segquant_gemm_workspace_bytes(M, N, K, len(wid), _arr_ptr(off),
+                                                            _arr_ptr(wid), flags))
+
+
 def segquant_gemm_w8a8_seg(x, w_packed, w_scale, act_scales, kseg: Optional[Sequence[int]] = None,
                            N: Optional[int] = None, xq=None, q_layout: int = SEGQ_Q_SIGNED,
-                           out=None, acc_debug=None, flags: int = SEGQ_GEMM_AUTO):
-    """The DualScale x SegLinear W8A8 layer in one launch.
+                           out=None, acc_debug=None, workspace="auto",
+                           flags: int = SEGQ_GEMM_AUTO):
+    """The DualScale x SegLinear W8A8 layer (one launch, or quantisation
+    then GEMM when a workspace is given and the library asks for one).
 
     x: bf16 [M][K] (or None with xq = the output of
     segquant_quantize_dualscale); w_packed/w_scale from
     segquant_quantize_weight; act_scales from segquant_calibrate_amax.
     Returns bf16 Y [M][N].  acc_debug, if given, is an int32 tensor
-    [2][n_kseg][M][N] that receives the per-segment accumulators."""
+    [2][n_kseg][M][N] that receives the per-segment accumulators.
+    workspace: a device tensor, None (always the fused launch), or "auto"
+    (a tensor of segquant_gemm_workspace_bytes() bytes from torch's
+    allocator when that is nonzero)."""
     import torch
     lib = load_library()
     src = x if x is not None else xq
@@ -250,9 +265,16 @@ def segquant_gemm_w8a8_seg(x, w_packed, w_scale, act_scales, kseg: Optional[Sequ
     off, wid = _segs(kseg, K)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=src.device)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be a tensor, None or 'auto'")
+        nb = segquant_gemm_workspace_bytes(M, N, K, kseg, flags) if x is not None else 0
+        workspace = torch.empty(nb, dtype=torch.uint8, device=src.device) if nb else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.segquant_gemm_w8a8_seg(M, N, K, _ptr(x), ld_x, _ptr(xq), ld_q, q_layout,
                                       _ptr(w_packed), _ptr(w_scale), len(wid), _arr_ptr(off),
                                       _arr_ptr(wid), _ptr(act_scales), _ptr(out), _ld(out, "out"),
-                                      _ptr(acc_debug), flags, _stream(src)),
+                                      _ptr(acc_debug), _ptr(workspace), ws_bytes, flags,
+                                      _stream(src)),
            "segquant_gemm_w8a8_seg")
     return out

@@ -210,7 +210,7 @@ static int gemm_check(int64_t M, int64_t N, int64_t K, uint32_t flags) {
   if (K % 64 || N % 16)
     return fail(SEGQ_ERR_ALIGN, "GEMM needs K %% 64 == 0 and N %% 16 == 0 (K=%lld N=%lld)",
                 (long long)K, (long long)N);
-  if (flags & ~(SEGQ_GEMM_FORCE_TILE | SEGQ_GEMM_FORCE_SMALLM))
+  if (flags & ~(SEGQ_GEMM_FORCE_TILE | SEGQ_GEMM_FORCE_SMALLM | SEGQ_GEMM_FUSED_QUANT))
     return fail(SEGQ_ERR_SHAPE, "unknown flags 0x%x", flags);
   if ((flags & SEGQ_GEMM_FORCE_TILE) && (flags & SEGQ_GEMM_FORCE_SMALLM))
     return fail(SEGQ_ERR_SHAPE, "both kernels forced");
@@ -228,6 +228,23 @@ int segquant_gemm_kernel_for(int64_t M, int64_t N, int64_t K, uint32_t flags) {
   return M <= sq::kSmallMMax ? SEGQ_KERNEL_SMALLM : SEGQ_KERNEL_TILE;
 }
 
+static bool quantize_first(int kernel, int64_t M, int64_t N, const sq::SegTable &ks,
+                           uint32_t flags) {
+  return kernel == SEGQ_KERNEL_TILE && !(flags & SEGQ_GEMM_FUSED_QUANT) &&
+         sq::tile_quantize_first(M, N, ks);
+}
+
+size_t segquant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t n_kseg,
+                                     const int32_t *kseg_offset, const int32_t *kseg_width,
+                                     uint32_t flags) {
+  if (gemm_check(M, N, K, flags)) return 0;
+  sq::SegTable ks{};
+  if (read_kseg(n_kseg, kseg_offset, kseg_width, K, SEGQ_MAX_KSEG_WIDTH, ks)) return 0;
+  ok();
+  const int kernel = segquant_gemm_kernel_for(M, N, K, flags);
+  return quantize_first(kernel, M, N, ks, flags) ? (size_t)(M * K) : 0;
+}
+
 int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
                            const uint16_t *x_bf16, int64_t ld_x,
                            const int8_t *xq, int64_t ld_q, int32_t q_layout,
@@ -235,6 +252,7 @@ int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
                            int32_t n_kseg, const int32_t *kseg_offset,
                            const int32_t *kseg_width, const float *act_scales,
                            uint16_t *y_bf16, int64_t ld_y, int32_t *acc_debug,
+                           void *workspace, size_t workspace_bytes,
                            uint32_t flags, void *stream) {
   int st = gemm_check(M, N, K, flags);
   if (st) return st;
@@ -258,6 +276,8 @@ int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
     if ((reinterpret_cast<uintptr_t>(y_bf16) & 1u) ||
         (acc_debug && (reinterpret_cast<uintptr_t>(acc_debug) & 3u)))
       return fail(SEGQ_ERR_ALIGN, "y_bf16 or acc_debug is misaligned");
+    if (workspace && !aligned16(workspace))
+      return fail(SEGQ_ERR_ALIGN, "workspace is not 16-byte aligned");
   }
   sq::SegTable ks{};
   if ((st = read_kseg(n_kseg, kseg_offset, kseg_width, K, SEGQ_MAX_KSEG_WIDTH, ks))) return st;
@@ -274,6 +294,19 @@ int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
   p.ks = ks;
   p.y = y_bf16; p.ld_y = ld_y; p.acc_debug = acc_debug;
   const int kernel = segquant_gemm_kernel_for(M, N, K, flags);
+  if (x_bf16 && workspace && quantize_first(kernel, M, N, ks, flags) &&
+      workspace_bytes >= (size_t)(M * K)) {
+    // quantise once into the workspace, then the GEMM from the signed codes
+    int8_t *codes = static_cast<int8_t *>(workspace);
+    hipError_t e = sq::launch_quantize(x_bf16, M, K, ld_x, ks, act_scales, codes, K,
+                                       SEGQ_Q_SIGNED, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "quantize launch");
+    p.x = nullptr;
+    p.ld_x = 0;
+    p.xq = codes;
+    p.ld_q = K;
+    p.q_layout = SEGQ_Q_SIGNED;
+  }
   hipError_t e = kernel == SEGQ_KERNEL_SMALLM ? sq::launch_gemm_smallm(p, (hipStream_t)stream)
                                               : sq::launch_gemm_tile(p, (hipStream_t)stream);
   return hip_status(e, "gemm launch");

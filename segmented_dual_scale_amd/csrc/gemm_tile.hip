@@ -674,6 +674,7 @@ hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s) {
   }
   const int amode = p.x ? A_BF16 : (p.q_layout == 1 ? A_PLANES : A_SIGNED);
   const bool debug = p.acc_debug != nullptr;
+  // (the tile widths here and in tile_columns() go together)
   if (p.ks.n == 1) return launch_variant<64, 384, SINGLE>(t, amode, debug, s);
   if (every_step) return launch_variant<32, 256, STEP>(t, amode, debug, s);
   bool even_ends = true;  // every segment end but the last on a whole stage
@@ -685,6 +686,21 @@ hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s) {
   hipLaunchKernelGGL(acc_difference_kernel, dim3((unsigned)((2 * mn + 255) / 256)), dim3(256), 0, s,
                      p.acc_debug, p.ks.n, mn);
   return hipGetLastError();
+}
+
+int tile_columns(const SegTable &ks) { return ks.n == 1 ? 384 : 256; }
+
+// With bf16 input the tile kernel quantises each activation tile once per
+// column tile, N / BN times over.  Quantising once into int8 codes instead
+// (one HBM pass: 2 bytes read and 1 written per element) and running the
+// GEMM from the codes costs less from about six column tiles on.  Measured
+// on MI355X: M=4429, K=1536, N=1536 in 24 K-segments (six tiles of 256)
+// 57 us against 67 us fused; M=9216, K=12288, N=3072 in 4 K-segments
+// (twelve tiles) 733 us against 991 us; M=4096, K=6144, N=1536 in one
+// segment (four tiles of 384) 84 us either way.
+bool tile_quantize_first(int64_t M, int64_t N, const SegTable &ks) {
+  const int bn = tile_columns(ks);
+  return M > kSmallMMax && (N + bn - 1) / bn >= 6;
 }
 
 }  // namespace sq

@@ -58,4 +58,10 @@ hipError_t launch_gemm_smallm(const GemmProblem &p, hipStream_t s);
 
 constexpr int kSmallMMax = 16;
 
+// Output columns per workgroup of the tile kernel for these K-segments.
+int tile_columns(const SegTable &ks);
+// Whether the tile kernel should run from int8 codes quantised beforehand
+// (one extra launch) rather than quantise bf16 input itself.
+bool tile_quantize_first(int64_t M, int64_t N, const SegTable &ks);
+
 }  // namespace sq

@@ -73,14 +73,14 @@ class GpuLayer:
         del wd
         torch.cuda.synchronize()
 
-    def run(self, mode="bf16", flags=S.SEGQ_GEMM_AUTO, debug=False):
+    def run(self, mode="bf16", flags=S.SEGQ_GEMM_AUTO, debug=False, workspace="auto"):
         import torch
         acc = None
         if debug:
             acc = torch.full((2, len(self.kseg), self.M, self.N), -7, dtype=torch.int32, device=DEV)
         if mode == "bf16":
             y = S.segquant_gemm_w8a8_seg(self.xd, self.wp, self.ws, self.act, self.kseg,
-                                         acc_debug=acc, flags=flags)
+                                         acc_debug=acc, workspace=workspace, flags=flags)
         else:
             layout = S.SEGQ_Q_SIGNED if mode == "signed" else S.SEGQ_Q_PLANES
             xq = S.segquant_quantize_dualscale(self.xd, self.act, self.kseg, layout)

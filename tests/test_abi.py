@@ -84,14 +84,15 @@ def segs(widths):
 
 
 def gemm(M=64, N=64, K=128, x=FAKE, ld_x=None, xq=None, ld_q=0, q_layout=0, w=FAKE, ws=FAKE,
-         widths=None, off=None, act=FAKE, y=FAKE, ld_y=None, acc=None, flags=0, n_kseg=None):
+         widths=None, off=None, act=FAKE, y=FAKE, ld_y=None, acc=None, flags=0, n_kseg=None,
+         work=None, work_bytes=0):
     o, wd = segs(widths if widths is not None else [K])
     if off is not None:
         o = np.asarray(off, np.int32)
     return lib().segquant_gemm_w8a8_seg(
         M, N, K, x, K if ld_x is None else ld_x, xq, ld_q, q_layout, w, ws,
         len(wd) if n_kseg is None else n_kseg, o.ctypes.data_as(P), wd.ctypes.data_as(P), act,
-        y, N if ld_y is None else ld_y, acc, flags, None)
+        y, N if ld_y is None else ld_y, acc, work, work_bytes, flags, None)
 
 
 @pytest.mark.parametrize("kwargs,status", [
@@ -134,9 +135,32 @@ def test_gemm_validation(kwargs, status):
     assert S.segquant_last_error() != ""
 
 
+def test_gemm_misaligned_workspace():
+    assert gemm(work=ctypes.c_void_p(0x10008), work_bytes=1 << 20) == S.SEGQ_ERR_ALIGN
+    assert "workspace" in S.segquant_last_error()
+
+
+@pytest.mark.parametrize("M,N,K,widths,flags,expect", [
+    (4096, 1536, 6144, None, 0, 0),                        # one segment: tiles of 384, 4 across
+    (4429, 1536, 1536, [64] * 24, 0, 4429 * 1536),         # tiles of 256, 6 across
+    (9216, 3072, 12288, [3072] * 4, 0, 9216 * 12288),      # 12 across
+    (9216, 3072, 12288, [3072] * 4, S.SEGQ_GEMM_FUSED_QUANT, 0),
+    (300, 2304, 512, None, 0, 300 * 512),                  # one segment, 6 tiles of 384
+    (300, 1920, 512, None, 0, 0),                          # 5 tiles
+    (16, 9216, 1536, None, 0, 0),                          # small M: the streaming kernel
+    (64, 9216, 1536, None, S.SEGQ_GEMM_FORCE_SMALLM, None),  # invalid: forced small-M, M > 16
+])
+def test_gemm_workspace_bytes(M, N, K, widths, flags, expect):
+    got = S.segquant_gemm_workspace_bytes(M, N, K, widths, flags)
+    if expect is None:
+        assert got == 0 and S.segquant_last_error() != ""
+    else:
+        assert got == expect and S.segquant_last_error() == ""
+
+
 def test_gemm_null_segment_arrays():
     rc = lib().segquant_gemm_w8a8_seg(64, 64, 128, FAKE, 128, None, 0, 0, FAKE, FAKE, 1, None,
-                                      None, FAKE, FAKE, 64, None, 0, None)
+                                      None, FAKE, FAKE, 64, None, None, 0, 0, None)
     assert rc == S.SEGQ_ERR_NULL
 
 

@@ -155,6 +155,49 @@ def test_gemm_parity(case, mode):
         assert ok, f"production Y out of tolerance (flags {flags}): {nbad} elements, worst {worst}"
 
 
+# Shapes for which the library quantises first when given a workspace (six or
+# more output column tiles): one segment (tiles of 384), every segment one
+# k-step (tiles of 256), general segments with an end inside a stage.
+QFIRST_CASES = [
+    # M, K, N, kseg
+    (300, 512, 2304, [512]),
+    (133, 640, 1536, [64] * 10),
+    (70, 1024, 1792, [320, 448, 256]),
+]
+
+
+@pytest.mark.parametrize("M,K,N,kseg", QFIRST_CASES)
+def test_gemm_quantize_first_parity(M, K, N, kseg):
+    """bf16 input with a workspace: one quantisation launch into the
+    workspace, then the GEMM from the codes.  The workspace ends up holding
+    the signed codes (so the two-launch path ran); accumulators bit-exact;
+    Y within tolerance; the fused launch (no workspace) agrees likewise."""
+    import torch
+    x, w = W.make_custom(M, K, N, seed=M + N, kind="blocks", x_scale=2.0)
+    ref = OracleLayer(x, w, kseg, None, True)
+    gpu = GpuLayer(x, w, kseg, None, True)
+    nb = S.segquant_gemm_workspace_bytes(M, N, K, kseg)
+    assert nb == M * K
+    for debug in (True, False):
+        work = torch.full((nb + 64,), 0x55, dtype=torch.uint8, device=DEV)
+        y, acc = gpu.run("bf16", debug=debug, workspace=work)
+        codes = work[:nb].view(torch.int8).view(M, K).cpu().numpy()
+        assert np.array_equal(np.maximum(codes, 0), ref.qp) and np.array_equal(np.minimum(codes, 0), ref.qn)
+        assert np.all(work[nb:].cpu().numpy() == 0x55), "write past the asked-for workspace"
+        if debug:
+            assert np.array_equal(acc.cpu().numpy(), ref.acc)
+        ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), ref.y)
+        assert ok, f"quantise-first Y out of tolerance: {nbad} elements, worst excess {worst}"
+    # too small a workspace, or the flag: the fused launch, which leaves it alone
+    for work_bytes, flags in ((nb - 16, S.SEGQ_GEMM_AUTO), (nb, S.SEGQ_GEMM_FUSED_QUANT)):
+        work = torch.full((work_bytes,), 0x55, dtype=torch.uint8, device=DEV)
+        y, acc = gpu.run("bf16", debug=True, workspace=work, flags=flags)
+        assert np.all(work.cpu().numpy() == 0x55)
+        assert np.array_equal(acc.cpu().numpy(), ref.acc)
+        ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), ref.y)
+        assert ok, f"fused Y out of tolerance: {nbad} elements, worst excess {worst}"
+
+
 def test_gemm_empty_batch_is_a_noop():
     import torch
     x, w = W.make_custom(4, 128, 32, seed=3)
@@ -198,13 +241,17 @@ def test_full_size_workload(name):
     assert np.array_equal(gpu.act.cpu().numpy().view(np.uint32), ref.act.view(np.uint32))
     assert np.array_equal(gpu.ws.cpu().numpy().view(np.uint32), ref.ws.view(np.uint32))
     assert np.array_equal(S.segquant_unpack_weight(gpu.wp, wl.K, wl.N).cpu().numpy(), ref.wq)
-    y, _ = gpu.run("bf16", debug=False)
     ymax = float(np.abs(ref.y).max())
-    ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y)[rows], ref.y, ymax)
-    assert ok, f"{name}: {nbad} sampled outputs out of tolerance, worst excess {worst}"
-    yd, acc = gpu.run("bf16", debug=True)
     ridx = torch.from_numpy(rows).to(DEV)
-    acc_rows = acc.index_select(2, ridx).cpu().numpy()
-    assert np.array_equal(acc_rows, ref.acc), f"{name}: int32 accumulators differ"
-    ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(yd)[rows], ref.y, ymax)
-    assert ok, f"{name}: accumulator-dumping variant out of tolerance, worst excess {worst}"
+    # as the benchmark calls it (a workspace when the library asks for one),
+    # and the fused launch
+    for flags in (S.SEGQ_GEMM_AUTO, S.SEGQ_GEMM_FUSED_QUANT):
+        y, _ = gpu.run("bf16", debug=False, flags=flags)
+        ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y)[rows], ref.y, ymax)
+        assert ok, f"{name} flags {flags}: {nbad} sampled outputs out of tolerance, worst {worst}"
+        yd, acc = gpu.run("bf16", debug=True, flags=flags)
+        acc_rows = acc.index_select(2, ridx).cpu().numpy()
+        del acc
+        assert np.array_equal(acc_rows, ref.acc), f"{name} flags {flags}: int32 accumulators differ"
+        ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(yd)[rows], ref.y, ymax)
+        assert ok, f"{name} flags {flags}: accumulator-dumping variant out of tolerance, worst {worst}"
