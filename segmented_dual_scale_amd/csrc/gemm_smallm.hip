@@ -268,7 +268,11 @@ struct StreamArgs {
 // QL: activation input, -1 bf16 (quantised here), 0 signed codes, 1 planes.
 // RING: weight tiles requested per wave, a multiple of 8 with K/64 <= RING.
 // SEG1: the call has one K-segment.
-template <int QL, int RING, bool SEG1, bool DEBUG>
+// PACK: M <= 8.  Both halves share one A operand: rows 0-7 hold the + plane
+// of rows 0-7 of X, rows 8-15 the - plane, so one matrix-core instruction
+// per weight tile computes both products (half the chain).  Otherwise each
+// half has its own A operand (rows at or past M zero).
+template <int QL, int RING, bool SEG1, bool PACK, bool DEBUG>
 __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t planes[2 * kSmallMMax * kStreamPitch];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -319,9 +323,10 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   const int8_t *wcol = a.w + (int64_t)ntc * KT * 1024 + lane * 16;
   v4u ring[RING];
 #pragma unroll
-  for (int d = 0; d < RING; ++d)
+  for (int d = 0; d < RING; ++d) {
     ring[d] = *reinterpret_cast<const v4u *>(wcol + (int64_t)min(d, KT - 1) * 1024);
-  __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);  // in tile order, as the chain below waits for them
+  }
 
 #pragma unroll
   for (int i = 0; i < kStreamXR; ++i) {
@@ -367,27 +372,72 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   }
   __syncthreads();
 
-  // (5) every A fragment of the call (rows at or past M are zero)
+  // (5) every A fragment of the call (rows at or past M are zero).  Lane l
+  //     supplies row l % 16, k-bytes 16 (l / 16) .. +16 of each k-tile.
   const int row = lane & 15, kq = (lane >> 4) * 16;
-  const bool row_ok = row < a.M;
-  v4u fa[RING], fb[RING];
+  const int xrow = PACK ? (row & 7) : row;  // PACK: rows 8-15 are the - plane's rows 0-7
+  const bool row_ok = xrow < a.M;
+  const uint8_t *fsrc = (PACK && row >= 8 ? pn : pp) + xrow * pitch + kq;
+  v4u fa[RING], fb[PACK ? 1 : RING];
 #pragma unroll
   for (int t = 0; t < RING; ++t) {
     fa[t] = v4u{0u, 0u, 0u, 0u};
-    fb[t] = v4u{0u, 0u, 0u, 0u};
+    if (!PACK) fb[PACK ? 0 : t] = v4u{0u, 0u, 0u, 0u};
   }
   if (row_ok) {  // the other lanes' rows are zero padding: no LDS traffic for them
     const int tmax = KT - 1;
 #pragma unroll
     for (int t = 0; t < RING; ++t) {
       const int tt = min(t, tmax);
-      fa[t] = *reinterpret_cast<const v4u *>(pp + row * pitch + tt * 64 + kq);
-      fb[t] = *reinterpret_cast<const v4u *>(pn + row * pitch + tt * 64 + kq);
+      fa[t] = *reinterpret_cast<const v4u *>(fsrc + tt * 64);
+      if (!PACK) fb[PACK ? 0 : t] = *reinterpret_cast<const v4u *>(pn + row * pitch + tt * 64 + kq);
+    }
+  }
+  // Ring slots past K hold a repeat of the last weight tile; their A
+  // fragments are zero, so they add nothing.  (Masking the A side, not the
+  // loaded weights: a select on a weight register would make the chain wait
+  // for that load early, and the compiler hoists such selects.)
+#pragma unroll
+  for (int t = RING - 7; t < RING; ++t) {
+    if (t < 0) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      fa[t][e] = t < KT ? fa[t][e] : 0u;
+      if (!PACK) fb[PACK ? 0 : t][e] = t < KT ? fb[PACK ? 0 : t][e] : 0u;
     }
   }
 
-  // (6) matrix-core chain as the weight tiles arrive; fold at segment ends
+  // (6) matrix-core chain as the weight tiles arrive; fold at segment ends.
+  //     The 16x16 result: lane l holds column l % 16, rows 4 (l / 16) + r.
   float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // segments fold in order: wsp[0] is this segment's scale; shift the queue
+  // and fetch the one kStreamPre segments ahead
+  auto next_wscale = [&](int seg) {
+    const float ws = wsp[0];
+#pragma unroll
+    for (int j = 0; j + 1 < kStreamPre; ++j) wsp[j] = wsp[j + 1];
+    if (!SEG1) wsp[kStreamPre - 1] = a.w_scale[(int64_t)min(seg + kStreamPre, nS - 1) * a.N + n];
+    return ws;
+  };
+  // PACK: lanes 0-31 hold the + products of rows 4 (l / 16) + r, lanes
+  // 32-63 the - products of the same rows; each lane scales its own half
+  // (the two partial sums are added across lanes at the end)
+  auto fold_packed = [&](int seg, const v4i &C) {
+    if (DEBUG) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = ((lane >> 4) & 1) * 4 + r;
+        if (active && m < a.M)
+          a.acc[((int64_t)((lane >> 5) * nS + seg) * a.M + m) * a.N + n] = C[r];
+      }
+    }
+    const float ws = next_wscale(seg);
+    const float sp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sp_l), seg));
+    const float sn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sn_l), seg));
+    const float c = (lane < 32 ? sp : sn) * ws;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(c, (float)C[r], yacc[r]);
+  };
   auto fold = [&](int seg, const v4i &P, const v4i &Q) {
     if (DEBUG) {
 #pragma unroll
@@ -400,12 +450,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
         }
       }
     }
-    // segments fold in order: wsp[0] is this segment's scale; shift the
-    // queue and fetch the one kStreamPre segments ahead
-    const float ws = wsp[0];
-#pragma unroll
-    for (int j = 0; j + 1 < kStreamPre; ++j) wsp[j] = wsp[j + 1];
-    if (!SEG1) wsp[kStreamPre - 1] = a.w_scale[(int64_t)min(seg + kStreamPre, nS - 1) * a.N + n];
+    const float ws = next_wscale(seg);
     const float sp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sp_l), seg));
     const float sn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sn_l), seg));
     const float cp = sp * ws, cn = sn * ws;
@@ -413,19 +458,30 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
     for (int r = 0; r < 4; ++r)
       yacc[r] = __builtin_fmaf(cn, (float)Q[r], __builtin_fmaf(cp, (float)P[r], yacc[r]));
   };
-  auto wtile = [&](int t) {
-    v4u b = ring[t];
-    if (t >= RING - 7) {  // the only slots that can lie past K
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b[e] = t < KT ? b[e] : 0u;
-    }
-    return b;
-  };
+  auto wtile = [&](int t) { return ring[t]; };
   auto mfma = [](const v4u &x, const v4u &w, const v4i &c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(reinterpret_cast<const v4i &>(x),
                                                  reinterpret_cast<const v4i &>(w), c, 0, 0, 0);
   };
-  if (SEG1) {
+  if (PACK && SEG1) {
+    // one instruction per tile, two independent chains (even, odd tiles)
+    v4i acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+    for (int t = 0; t < RING; ++t) acc[t & 1] = mfma(fa[t], wtile(t), acc[t & 1]);
+    fold_packed(0, acc[0] + acc[1]);
+  } else if (PACK) {
+    v4i acc = {0, 0, 0, 0};
+    int seg = 0;
+#pragma unroll
+    for (int t = 0; t < RING; ++t) {
+      acc = mfma(fa[t], wtile(t), acc);
+      if ((a.fold_mask >> t) & 1u) {
+        fold_packed(seg, acc);
+        acc = v4i{0, 0, 0, 0};
+        ++seg;
+      }
+    }
+  } else if (SEG1) {
     // one K-segment: no fold until the end, so the chain is branch-free; even
     // and odd k-tiles accumulate separately (two independent chains per
     // half) and are added at the end (exact in int32)
@@ -434,7 +490,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
     for (int t = 0; t < RING; ++t) {
       const v4u b = wtile(t);
       acc[(t & 1) * 2] = mfma(fa[t], b, acc[(t & 1) * 2]);
-      acc[(t & 1) * 2 + 1] = mfma(fb[t], b, acc[(t & 1) * 2 + 1]);
+      acc[(t & 1) * 2 + 1] = mfma(fb[PACK ? 0 : t], b, acc[(t & 1) * 2 + 1]);
     }
     fold(0, acc[0] + acc[2], acc[1] + acc[3]);
   } else {
@@ -444,7 +500,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
     for (int t = 0; t < RING; ++t) {
       const v4u b = wtile(t);
       accp = mfma(fa[t], b, accp);
-      accn = mfma(fb[t], b, accn);
+      accn = mfma(fb[PACK ? 0 : t], b, accn);
       if ((a.fold_mask >> t) & 1u) {
         fold(seg, accp, accn);
         accp = v4i{0, 0, 0, 0};
@@ -454,18 +510,25 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
     }
   }
 
-  // epilogue: rows (lane/16)*4 + r of column n
+  // epilogue: rows (lane/16)*4 + r of column n (PACK: lanes 0-31, after
+  // adding the - half's sums from lane l + 32)
+  if (PACK) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yacc[r] += __shfl_down(yacc[r], 32, 64);
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = (lane >> 4) * 4 + r;
-    if (active && m < a.M) a.y[(int64_t)m * a.ld_y + n] = (uint16_t)f32_to_bf16_rne(yacc[r]);
+    if (active && m < a.M && (!PACK || lane < 32))
+      a.y[(int64_t)m * a.ld_y + n] = (uint16_t)f32_to_bf16_rne(yacc[r]);
   }
 }
 
-template <int RING, bool SEG1>
+template <int RING, bool SEG1, bool PACK>
 void launch_stream_ring(const StreamArgs &a, int ql, bool debug, dim3 grid, hipStream_t s) {
-#define SQ_STREAM(QLV, DBG) \
-  hipLaunchKernelGGL((gemm_smallm_kernel<QLV, RING, SEG1, DBG>), grid, dim3(kStreamThreads), 0, s, a)
+#define SQ_STREAM(QLV, DBG)                                                                   \
+  hipLaunchKernelGGL((gemm_smallm_kernel<QLV, RING, SEG1, PACK, DBG>), grid, dim3(kStreamThreads), \
+                     0, s, a)
   if (debug) {
     if (ql < 0) SQ_STREAM(-1, true);
     else if (ql == 0) SQ_STREAM(0, true);
@@ -480,8 +543,14 @@ void launch_stream_ring(const StreamArgs &a, int ql, bool debug, dim3 grid, hipS
 
 template <int RING>
 void launch_stream_segs(const StreamArgs &a, int ql, bool debug, dim3 grid, hipStream_t s) {
-  if (a.n_kseg == 1) launch_stream_ring<RING, true>(a, ql, debug, grid, s);
-  else launch_stream_ring<RING, false>(a, ql, debug, grid, s);
+  const bool pack = a.M <= 8;
+  if (a.n_kseg == 1) {
+    if (pack) launch_stream_ring<RING, true, true>(a, ql, debug, grid, s);
+    else launch_stream_ring<RING, true, false>(a, ql, debug, grid, s);
+  } else {
+    if (pack) launch_stream_ring<RING, false, true>(a, ql, debug, grid, s);
+    else launch_stream_ring<RING, false, false>(a, ql, debug, grid, s);
+  }
 }
 
 // Shapes the streaming kernel takes; the rest go to the chunked kernel.

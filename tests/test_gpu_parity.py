@@ -115,6 +115,9 @@ GEMM_CASES = [
     (1, 64, 16, [64], [16], False, "gelu"),
     (2, 1536, 576, [1536], [96] * 6, False, "silu"),
     (3, 256, 48, [64, 192], None, True, "blocks"),
+    (8, 512, 112, [128, 384], None, True, "blocks"),   # largest M with both halves in one operand
+    (5, 2048, 64, [64] * 32, [64], False, "blocks"),    # 32 segments, the full weight ring
+    (9, 1024, 160, [1024], [160], False, "gelu"),       # smallest M with an operand per half
     (16, 640, 256, [64] * 10, [256], False, "blocks"),
     (17, 256, 272, [256], None, True, "gelu"),
     (77, 384, 768, [128, 256], [256] * 3, False, "gelu"),
