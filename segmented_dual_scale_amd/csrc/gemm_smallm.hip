@@ -268,10 +268,13 @@ struct StreamArgs {
 // QL: activation input, -1 bf16 (quantised here), 0 signed codes, 1 planes.
 // RING: weight tiles requested per wave, a multiple of 8 with K/64 <= RING.
 // SEG1: the call has one K-segment.
-// PACK: M <= 8.  Both halves share one A operand: rows 0-7 hold the + plane
-// of rows 0-7 of X, rows 8-15 the - plane, so one matrix-core instruction
-// per weight tile computes both products (half the chain).  Otherwise each
-// half has its own A operand (rows at or past M zero).
+// PACK: M <= 8.  Both halves share one A operand, in groups of four rows:
+// rows 4j, 4j+1 hold the + plane of X rows 2j, 2j+1 and rows 4j+2, 4j+3 their
+// - plane.  One matrix-core instruction per weight tile then computes both
+// products (half the chain), and since a lane's four result registers are
+// four consecutive rows, each lane holds both halves of its two X rows: the
+// fold needs no data from other lanes.  Otherwise each half has its own A
+// operand (rows at or past M zero).
 template <int QL, int RING, bool SEG1, bool PACK, bool DEBUG>
 __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t planes[2 * kSmallMMax * kStreamPitch];
@@ -375,9 +378,10 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   // (5) every A fragment of the call (rows at or past M are zero).  Lane l
   //     supplies row l % 16, k-bytes 16 (l / 16) .. +16 of each k-tile.
   const int row = lane & 15, kq = (lane >> 4) * 16;
-  const int xrow = PACK ? (row & 7) : row;  // PACK: rows 8-15 are the - plane's rows 0-7
+  // PACK: operand row 4j + p is X row 2j + (p & 1), - plane when p >= 2
+  const int xrow = PACK ? ((row >> 2) << 1) + (row & 1) : row;
   const bool row_ok = xrow < a.M;
-  const uint8_t *fsrc = (PACK && row >= 8 ? pn : pp) + xrow * pitch + kq;
+  const uint8_t *fsrc = (PACK && (row & 2) ? pn : pp) + xrow * pitch + kq;
   v4u fa[RING], fb[PACK ? 1 : RING];
 #pragma unroll
   for (int t = 0; t < RING; ++t) {
@@ -419,24 +423,24 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
     if (!SEG1) wsp[kStreamPre - 1] = a.w_scale[(int64_t)min(seg + kStreamPre, nS - 1) * a.N + n];
     return ws;
   };
-  // PACK: lanes 0-31 hold the + products of rows 4 (l / 16) + r, lanes
-  // 32-63 the - products of the same rows; each lane scales its own half
-  // (the two partial sums are added across lanes at the end)
+  // PACK: lane l holds, for column n and X rows 2j, 2j+1 (j = l / 16), the
+  // + products in registers 0, 1 and the - products in registers 2, 3
   auto fold_packed = [&](int seg, const v4i &C) {
     if (DEBUG) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = ((lane >> 4) & 1) * 4 + r;
+        const int m = (lane >> 4) * 2 + (r & 1);
         if (active && m < a.M)
-          a.acc[((int64_t)((lane >> 5) * nS + seg) * a.M + m) * a.N + n] = C[r];
+          a.acc[((int64_t)((r >> 1) * nS + seg) * a.M + m) * a.N + n] = C[r];
       }
     }
     const float ws = next_wscale(seg);
     const float sp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sp_l), seg));
     const float sn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sn_l), seg));
-    const float c = (lane < 32 ? sp : sn) * ws;
+    const float cp = sp * ws, cn = sn * ws;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(c, (float)C[r], yacc[r]);
+    for (int r = 0; r < 2; ++r)
+      yacc[r] = __builtin_fmaf(cn, (float)C[r + 2], __builtin_fmaf(cp, (float)C[r], yacc[r]));
   };
   auto fold = [&](int seg, const v4i &P, const v4i &Q) {
     if (DEBUG) {
@@ -510,17 +514,11 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
     }
   }
 
-  // epilogue: rows (lane/16)*4 + r of column n (PACK: lanes 0-31, after
-  // adding the - half's sums from lane l + 32)
-  if (PACK) {
+  // epilogue: rows (lane/16)*4 + r of column n (PACK: rows (lane/16)*2 + r)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) yacc[r] += __shfl_down(yacc[r], 32, 64);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = (lane >> 4) * 4 + r;
-    if (active && m < a.M && (!PACK || lane < 32))
-      a.y[(int64_t)m * a.ld_y + n] = (uint16_t)f32_to_bf16_rne(yacc[r]);
+  for (int r = 0; r < (PACK ? 2 : 4); ++r) {
+    const int m = (lane >> 4) * (PACK ? 2 : 4) + r;
+    if (active && m < a.M) a.y[(int64_t)m * a.ld_y + n] = (uint16_t)f32_to_bf16_rne(yacc[r]);
   }
 }
 

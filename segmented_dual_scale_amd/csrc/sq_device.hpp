@@ -99,11 +99,13 @@ __device__ __forceinline__ void split_signed(uint32_t q, uint32_t &pos, uint32_t
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite values; NaN stays NaN).
+// A select, not a branch: in a store epilogue the branch cost more than the
+// arithmetic.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return (u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
