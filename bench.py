@@ -273,6 +273,89 @@ class Layer:
         self.xs = self.xqs = self.wps = self.ys = self.work = None
 
 
+def measured_peaks(dev, stream):
+    """Ceilings measured on this GPU by the probe library: an int8
+    matrix-core-only loop (one wave per SIMD and two), the shader clock while
+    it runs, a streaming read and a device copy of 1 GiB."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "segmented_dual_scale_amd", "libsegquant_probe.so")
+    lib = ctypes.CDLL(path)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.sqprobe_mfma_i8.argtypes = [I64, I32, I32, P, P, P]
+    lib.sqprobe_stream_read.argtypes = [P, I64, I32, P, P]
+    lib.sqprobe_ops_per_mfma.restype = I64
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    khz = lib.sqprobe_wall_clock_khz()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        return best
+
+    out = {}
+    iters = 40000
+    best_tops, clock = 0.0, None
+    for blocks_per_cu in (1, 2):
+        blocks = cus * blocks_per_cu
+        waves = blocks * 4
+        sink = torch.empty(waves * 64, dtype=torch.int32, device=dev)
+        spans = torch.zeros(waves * 2, dtype=torch.int64, device=dev)
+
+        def run():
+            rc = lib.sqprobe_mfma_i8(iters, blocks, 4, ctypes.c_void_p(sink.data_ptr()),
+                                     ctypes.c_void_p(spans.data_ptr()), sp)
+            if rc != 0:
+                raise RuntimeError(f"sqprobe_mfma_i8 failed ({rc})")
+        with torch.cuda.stream(stream):
+            t = timed(run, 3)
+        ops = waves * iters * lib.sqprobe_mfma_chains() * lib.sqprobe_ops_per_mfma()
+        tops = ops / t / 1e12
+        sv = spans.view(-1, 2).cpu().double()
+        ratio = float((sv[:, 0] / sv[:, 1].clamp(min=1)).median())
+        out[f"mfma_loop_{blocks_per_cu}wg_per_cu_tops"] = tops
+        if tops > best_tops:
+            best_tops = tops
+            clock = ratio * khz * 1e3 if khz > 0 else None
+    out["int8_mfma_tops"] = best_tops
+    out["shader_clock_ghz_under_mfma"] = clock / 1e9 if clock else None
+    nbytes = 1 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    blocks = cus * 8
+    rsink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+
+    def read():
+        rc = lib.sqprobe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, blocks,
+                                     ctypes.c_void_p(rsink.data_ptr()), sp)
+        if rc != 0:
+            raise RuntimeError(f"sqprobe_stream_read failed ({rc})")
+    with torch.cuda.stream(stream):
+        t = timed(read, 5)
+    out["hbm_read_gbs"] = nbytes / t / 1e9
+    half = nbytes // 2
+    src, dst = buf[:half], buf[half:]
+    with torch.cuda.stream(stream):
+        t = timed(lambda: dst.copy_(src), 5)
+    out["hbm_copy_gbs"] = 2 * half / t / 1e9
+    out["method"] = (f"probe library: int8 32x32x32 matrix-core loop, {lib.sqprobe_mfma_chains()} "
+                     f"independent accumulators per wave, 4 waves per workgroup, 1 and 2 "
+                     f"workgroups per CU ({cus} CUs), clock = shader/constant clock ratio "
+                     f"over the loop; grid-stride 16-byte read of 1 GiB; torch copy of 512 MiB; "
+                     f"best of 3-5 timed launches")
+    del buf, rsink
+    return out
+
+
 def copy_probe(dev, reps: int = 3):
     """A copy of known size (the scale of the FETCH_SIZE / WRITE_SIZE counters)."""
     import torch
@@ -358,6 +441,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch each step from Python")
     ap.add_argument("--no-all", action="store_true", help="skip the all_workloads summary")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured ceilings (matrix-core loop, streaming read)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="a few plain steps of --workload, then the copy probe (run under "
                          "rocprofv3 --pmc)")
@@ -463,6 +548,14 @@ def main():
             del lay
             torch.cuda.empty_cache()
         line["all_workloads"] = summary
+    if not args.no_peaks:
+        mp = measured_peaks(dev, stream)
+        line["measured_peaks"] = mp
+        ref = mp["hbm_read_gbs"] if roof["bound"] == "hbm" else mp["int8_mfma_tops"]
+        roof["frac_of_measured"] = roof["achieved"] / ref
+        for v in line.get("all_workloads", {}).values():
+            ref = mp["hbm_read_gbs"] if v["bound"] == "hbm" else mp["int8_mfma_tops"]
+            v["frac_of_measured"] = v["value"] / ref
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, x_host, w_host)
     print(json.dumps(line), flush=True)

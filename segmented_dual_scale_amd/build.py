@@ -20,6 +20,10 @@ OUT = os.path.join(HERE, "libsegquant.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "act_kernels.hip", "weight_kernels.hip", "gemm_tile.hip", "gemm_smallm.hip"]
+# ceiling probes for the benchmark (matrix-core-only loop, streaming read):
+# a library of their own, not part of the layer's
+PROBE_SOURCES = ["probes.hip"]
+PROBE_OUT = os.path.join(HERE, "libsegquant_probe.so")
 
 ARCH = os.environ.get("SEGQUANT_ARCH", "gfx950")
 
@@ -54,14 +58,19 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             print(r.stderr, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(PROBE_SOURCES))) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+
+    def link(out, parts):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *parts]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, out)
+
+    link(OUT, objs[:len(SOURCES)])
+    link(PROBE_OUT, objs[len(SOURCES):])
     return OUT
 
 
