@@ -105,6 +105,14 @@ constexpr int pieces_in_sub(int xp, int ks) {
   return n;
 }
 
+// With bf16 input in the single-segment loop (three activation slots, four
+// pieces a stage) the quantisation is spread over all four sub-blocks: pieces
+// 0-2 of stage u + 1 in sub-blocks 0-2 of stage u, and piece 3 of stage u + 2
+// in sub-block 3 (after the barrier; its buffer was last read in stage u - 1).
+// Each sub-block then carries one piece's vector ALU work beside its twelve
+// matrix-core instructions instead of two, one, one and none.
+constexpr bool spread_quant(int mode, int amode, int xp) { return mode == 0 && amode == 0 && xp == 4; }
+
 // Segment end i, read straight from the kernel-argument segment (the
 // argument is the only one, at offset 0).  Indexing the by-value argument
 // itself with a run-time index would make the compiler copy all of it into
@@ -203,6 +211,7 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
   // memory latency hidden).  Three for the single-segment loop; the fold
   // modes need the registers and keep two.
   constexpr int XS = MODE == SINGLE ? 3 : 2;
+  constexpr bool SPREAD = spread_quant(MODE, AMODE, XP);
   v4u xr[XS][XP];
   auto load_x = [&](auto SLOT, int u) __attribute__((always_inline)) {
     constexpr int s = decltype(SLOT)::value;
@@ -438,6 +447,8 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
     }
 #pragma unroll
     for (int i = 0; i < XP; ++i) quant_piece(ic<0>{}, i, smem, ip, in, my_half < KT);
+    // (spread: piece 3 of stage 1 belongs to the sub-block 3 of a stage -1)
+    if (SPREAD) quant_piece(ic<1>{}, XP - 1, smem + A_STAGE, ip, in, 2 + my_half < KT);
   }
   __syncthreads();
   read_frags(ic<0>{}, smem, 0);
@@ -506,16 +517,26 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
         load_w1(ic<s>{}, nb, ks, u + 2);  // refill with the stage two ahead
       }
       // this sub-block's share of the quantisation of stage u + 1
+      if (SPREAD) {
+        if (ks < 3) {
+          quant_piece(ic<x_quant>{}, ks, wrb, q_ip, q_in, q_valid);
+        } else {  // piece 3 of stage u + 2: slot and buffer (u + 2) % 3
+          uint8_t *wrb2 = smem + (b_rd == 0 ? 2 : b_rd - 1) * A_STAGE;
+          quant_piece(ic<SPREAD ? (s3 + 2) % 3 : 0>{}, XP - 1, wrb2, q_ip, q_in,
+                      2 * (u + 2) + my_half < KT);
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < XP; ++i)
-        if ((i * 3) / XP == ks) quant_piece(ic<x_quant>{}, i, wrb, q_ip, q_in, q_valid);
+        for (int i = 0; i < XP; ++i)
+          if ((i * 3) / XP == ks) quant_piece(ic<x_quant>{}, i, wrb, q_ip, q_in, q_valid);
+      }
       {
         // Interleave: one matrix-core instruction, then an even share of the
         // vector ALU work (quantisation), the weight refills spread among
         // them, the LDS writes last.  Without it the ALU work comes in
         // clumps of ~100 instructions during which the matrix cores idle.
         constexpr int NMF = 2 * MB * NB;
-        constexpr int nq = pieces_in_sub(XP, ks);
+        constexpr int nq = SPREAD ? 1 : pieces_in_sub(XP, ks);
         constexpr int vpq = AMODE == A_BF16 ? 56 : AMODE == A_SIGNED ? 16 : 0;
         constexpr int vfold = (MODE == STEP && (ks & 1)) ? MB * NB * 16 * 4 : 0;
         constexpr int per = (nq * vpq + vfold + NMF - 1) / NMF + 1;

@@ -118,6 +118,8 @@ GEMM_CASES = [
     (8, 512, 112, [128, 384], None, True, "blocks"),   # largest M with both halves in one operand
     (5, 2048, 64, [64] * 32, [64], False, "blocks"),    # 32 segments, the full weight ring
     (9, 1024, 160, [1024], [160], False, "gelu"),       # smallest M with an operand per half
+    (40, 320, 96, [320], None, True, "gelu"),           # one segment, odd number of k-tiles
+    (70, 192, 400, [192], [400], False, "silu"),        # one segment, three k-tiles, ragged N
     (16, 640, 256, [64] * 10, [256], False, "blocks"),
     (17, 256, 272, [256], None, True, "gelu"),
     (77, 384, 768, [128, 256], [256] * 3, False, "gelu"),
