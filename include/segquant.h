@@ -87,6 +87,7 @@ extern "C" {
 #define SEGQ_GEMM_FORCE_SMALLM 2u /* the weight-streaming kernel (M <= 16) */
 #define SEGQ_GEMM_FUSED_QUANT 4u  /* quantise bf16 input inside the GEMM kernel
                                      even when a workspace is given */
+#define SEGQ_GEMM_SINGLE_SCALE 8u /* single-scale W8A8: see segquant_gemm_w8a8_seg */
 
 /* Kernel choices reported by segquant_gemm_kernel_for. */
 #define SEGQ_KERNEL_TILE 1
@@ -108,6 +109,24 @@ extern "C" {
 int segquant_calibrate_amax(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ld_x,
                             int32_t n_kseg, const int32_t *kseg_offset,
                             const int32_t *kseg_width, float *act_scales, void *stream);
+
+/*
+ * segquant_calibrate_amax_single -- the single-scale baseline's calibration
+ * [P2 deployment-cost table, INT8 baseline row; P1 limitations section:
+ * DualScale doubles the products, so it may be enabled only for layers whose
+ * activations are polarity-asymmetric].  Per K-segment i, one symmetric
+ * range a = max(max x, -min x) over X[:, segment i]:
+ *   s = a/127, inv = 127/a (fp64 quotients rounded once to fp32; 0 when a = 0)
+ * written into BOTH halves of the table (s_pos = s_neg = s, inv_pos =
+ * inv_neg = inv).  With such a table the DualScale quantiser yields the
+ * plain symmetric codes clamp(rne(fp32(x * inv)), -127, 127), and the layer
+ * equals textbook per-segment W8A8; SEGQ_GEMM_SINGLE_SCALE then computes it
+ * with one product instead of two.  Arguments and launches as
+ * segquant_calibrate_amax.
+ */
+int segquant_calibrate_amax_single(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ld_x,
+                                   int32_t n_kseg, const int32_t *kseg_offset,
+                                   const int32_t *kseg_width, float *act_scales, void *stream);
 
 /*
  * segquant_quantize_dualscale -- polarity split and dual-scale quantisation
@@ -193,7 +212,17 @@ int segquant_unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t 
  *              (same stream).  NULL, or fewer bytes than asked for: one
  *              fused launch.
  *   flags      SEGQ_GEMM_AUTO, or force one kernel for testing
- *              (SEGQ_GEMM_FUSED_QUANT: never use the workspace).
+ *              (SEGQ_GEMM_FUSED_QUANT: never use the workspace), or'ed with
+ *              SEGQ_GEMM_SINGLE_SCALE: single-scale W8A8.  Only the + half
+ *              of act_scales is read: each element is quantised with inv_pos
+ *              of its segment (code in [-128, 127]) and
+ *                y[m][n] = bf16( sum_i w_scale[i][n] * s_pos[i] * A_i[m][n] )
+ *              with A_i the exact int32 product of the signed codes: one
+ *              product per element instead of two.  With a table from
+ *              segquant_calibrate_amax_single this is the DualScale formula
+ *              of that table.  acc_debug then receives A_i in plane 0 and
+ *              plane 1 is not written.  Takes bf16 or SEGQ_Q_SIGNED input
+ *              (SEGQ_Q_PLANES: SEGQ_ERR_UNSUPPORTED).
  * Requires K % 64 == 0, N % 16 == 0, every K-segment width <=
  * SEGQ_MAX_KSEG_WIDTH (and, with more than one K-segment, K itself <=
  * SEGQ_MAX_KSEG_WIDTH: SEGQ_ERR_UNSUPPORTED otherwise, as the large-M kernel

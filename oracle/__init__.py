@@ -54,12 +54,14 @@ def _load():
     lib.oracle_polarity_split.restype = None
     lib.oracle_polarity_split.argtypes = [P, I64, P, P]
     lib.oracle_calibrate_amax.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, P]
+    lib.oracle_calibrate_amax_single.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, P]
     lib.oracle_quantize_dualscale.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, P]
     lib.oracle_quantize_weight.argtypes = [P, I64, I64, I64, I32, P, P, I32, P, P, I32, P, P]
     lib.oracle_segment_acc.argtypes = [P, P, P, I64, I64, I64, I32, P, P, P]
     lib.oracle_dequantize.argtypes = [P, I64, I64, I32, P, P, P, P]
     lib.oracle_dualscale_linear.argtypes = [P, I64, I64, I64, P, P, I64, I32, P, P, P, P, P, P, P]
-    for f in ("oracle_calibrate_amax", "oracle_quantize_dualscale", "oracle_quantize_weight",
+    for f in ("oracle_calibrate_amax", "oracle_calibrate_amax_single",
+              "oracle_quantize_dualscale", "oracle_quantize_weight",
               "oracle_segment_acc", "oracle_dequantize", "oracle_dualscale_linear"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
@@ -103,6 +105,17 @@ def calibrate_amax(x_bf16: np.ndarray, kseg: Sequence[int]):
     out = [np.empty(len(wid), np.float32) for _ in range(4)]
     _check(_load().oracle_calibrate_amax(_ptr(x), M, K, K, len(wid), _ptr(off), _ptr(wid),
                                          *[_ptr(o) for o in out]), "calibrate_amax")
+    return tuple(out)
+
+
+def calibrate_amax_single(x_bf16: np.ndarray, kseg: Sequence[int]):
+    """Single-scale table: (s, s, inv, inv) per K-segment, s = max|x|/127."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M, K = x.shape
+    off, wid = _segs(kseg)
+    out = [np.empty(len(wid), np.float32) for _ in range(4)]
+    _check(_load().oracle_calibrate_amax_single(_ptr(x), M, K, K, len(wid), _ptr(off), _ptr(wid),
+                                                *[_ptr(o) for o in out]), "calibrate_amax_single")
     return tuple(out)
 
 

@@ -133,6 +133,35 @@ int oracle_calibrate_amax(const uint16_t *x, int64_t M, int64_t K, int64_t ld,
   return ORACLE_OK;
 }
 
+/* ------------------------------------------------------------------------
+ * Single-scale calibration, the plain W8A8 baseline that DualScale is
+ * measured against  [P2 deployment-cost table, INT8 baseline row; P1
+ * limitations section: DualScale could be enabled per layer only where the
+ * polarity asymmetry is strong].  Per K-segment i one symmetric range:
+ *   a = max(max x, -min x)   over X[:, segment i]
+ *   s = a / 127, inv = 127 / a   (range_scale; zero range gives 0)
+ * stored in both halves (s+ = s- = s, inv+ = inv- = inv), so that the
+ * dual-scale quantisation below produces clamp(rne(fp32(x * inv)),
+ * -127, 127) and the dequantisation the single-scale sum.
+ * ---------------------------------------------------------------------- */
+int oracle_calibrate_amax_single(const uint16_t *x, int64_t M, int64_t K, int64_t ld,
+                                 int32_t n_kseg, const int32_t *koff, const int32_t *kwid,
+                                 float *s_pos, float *s_neg, float *inv_pos, float *inv_neg) {
+  if (M < 0 || K < 1 || ld < K || !segs_ok(n_kseg, koff, kwid, K)) return ORACLE_ERR_ARG;
+  for (int32_t i = 0; i < n_kseg; ++i) {
+    double a = 0.0;
+    for (int64_t m = 0; m < M; ++m)
+      for (int64_t k = koff[i]; k < (int64_t)koff[i] + kwid[i]; ++k) {
+        double v = fabs((double)bf16_to_f32(x[m * ld + k]));
+        if (v > a) a = v;
+      }
+    range_scale(a, 127.0, &s_pos[i], &inv_pos[i]);
+    s_neg[i] = s_pos[i];
+    inv_neg[i] = inv_pos[i];
+  }
+  return ORACLE_OK;
+}
+
 /* One half's code: rne of the fp32 product (R2, R3), then clamp (R4).
  * A zero inverse means a zero range: that half is all zeros (R5). */
 static int32_t quant_code(float v_half, float inv, int32_t lo, int32_t hi) {

@@ -29,7 +29,8 @@ __all__ = [
     "segquant_quantize_weight", "segquant_unpack_weight", "segquant_gemm_w8a8_seg",
     "segquant_gemm_kernel_for", "segquant_status_string", "segquant_last_error",
     "segquant_version", "SEGQ_Q_SIGNED", "SEGQ_Q_PLANES", "SEGQ_GEMM_AUTO",
-    "SEGQ_GEMM_FORCE_TILE", "SEGQ_GEMM_FORCE_SMALLM", "SEGQ_GEMM_FUSED_QUANT", "SEGQ_KERNEL_TILE", "SEGQ_KERNEL_SMALLM",
+    "SEGQ_GEMM_FORCE_TILE", "SEGQ_GEMM_FORCE_SMALLM", "SEGQ_GEMM_FUSED_QUANT",
+    "SEGQ_GEMM_SINGLE_SCALE", "segquant_calibrate_amax_single", "SEGQ_KERNEL_TILE", "SEGQ_KERNEL_SMALLM",
 ]
 
 SEGQ_OK = 0
@@ -47,6 +48,7 @@ SEGQ_GEMM_AUTO = 0
 SEGQ_GEMM_FORCE_TILE = 1
 SEGQ_GEMM_FORCE_SMALLM = 2
 SEGQ_GEMM_FUSED_QUANT = 4
+SEGQ_GEMM_SINGLE_SCALE = 8
 SEGQ_KERNEL_TILE = 1
 SEGQ_KERNEL_SMALLM = 2
 
@@ -77,6 +79,7 @@ def load_library():
     P, I64, I32, U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
     sig = {
         "segquant_calibrate_amax": [P, I64, I64, I64, I32, P, P, P, P],
+        "segquant_calibrate_amax_single": [P, I64, I64, I64, I32, P, P, P, P],
         "segquant_quantize_dualscale": [P, I64, I64, I64, I32, P, P, P, P, I64, I32, P],
         "segquant_quantize_weight": [P, I64, I64, I64, I32, P, P, I32, P, P, I32, P, P, P],
         "segquant_unpack_weight": [P, I64, I64, P, I64, P],
@@ -156,19 +159,30 @@ def segquant_gemm_kernel_for(M: int, N: int, K: int, flags: int = SEGQ_GEMM_AUTO
     return int(load_library().segquant_gemm_kernel_for(M, N, K, flags))
 
 
-def segquant_calibrate_amax(x, kseg: Optional[Sequence[int]] = None, out=None):
-    """AMax calibration: returns the fp32 [4][n_kseg] table (s+, s-, inv+,
-    inv-) for bf16 X [M][K] (device)."""
+def _calibrate(fn, name, x, kseg, out):
     import torch
-    lib = load_library()
     M, K = x.shape
     off, wid = _segs(kseg, K)
     if out is None:
         out = torch.empty((4, len(wid)), dtype=torch.float32, device=x.device)
-    _check(lib.segquant_calibrate_amax(_ptr(x), M, K, _ld(x, "x"), len(wid), _arr_ptr(off),
-                                       _arr_ptr(wid), _ptr(out), _stream(x)),
-           "segquant_calibrate_amax")
+    _check(fn(_ptr(x), M, K, _ld(x, "x"), len(wid), _arr_ptr(off), _arr_ptr(wid), _ptr(out),
+              _stream(x)), name)
     return out
+
+
+def segquant_calibrate_amax(x, kseg: Optional[Sequence[int]] = None, out=None):
+    """AMax calibration: returns the fp32 [4][n_kseg] table (s+, s-, inv+,
+    inv-) for bf16 X [M][K] (device)."""
+    return _calibrate(load_library().segquant_calibrate_amax, "segquant_calibrate_amax", x, kseg,
+                      out)
+
+
+def segquant_calibrate_amax_single(x, kseg: Optional[Sequence[int]] = None, out=None):
+    """Single-scale calibration: the same table layout with s+ = s- =
+    max|x|/127 and inv+ = inv- = 127/max|x| per K-segment (use with
+    SEGQ_GEMM_SINGLE_SCALE)."""
+    return _calibrate(load_library().segquant_calibrate_amax_single,
+                      "segquant_calibrate_amax_single", x, kseg, out)
 
 
 def segquant_quantize_dualscale(x, act_scales, kseg: Optional[Sequence[int]] = None,

@@ -2,6 +2,11 @@
 //   * AMax calibration of the static DualScale scales
 //     [P1 framework table, AMax calibrator; P1 "DualScale" scale equation;
 //      P2 section 3, s+ = max/127 and s- = |min|/128], and
+//   * the single-scale variant of the calibration (one symmetric scale per
+//     K-segment, amax/127, written into both halves of the table): the
+//     plain W8A8 baseline that DualScale is compared with [P2 deployment-cost
+//     table, INT8 baseline row; P1 limitations section, enabling DualScale
+//     only where the polarity asymmetry calls for it], and
 //   * the standalone polarity split + dual-scale quantisation
 //     [P1 "DualScale" split and quantisation; P2 section 3, Q_dual], an
 //     HBM-streaming kernel: 2 bytes read and 1 (signed code) or 2 (two
@@ -34,6 +39,7 @@ struct ActArgs {
   int64_t ld_q;
   int64_t plane_stride;  // elements between the + and - planes (0: signed)
   int32_t n_kseg;
+  int32_t single;        // quantise both signs with the + half's inverse
   SegTable ks;
 };
 
@@ -85,13 +91,23 @@ __global__ __launch_bounds__(256) void calib_reduce_kernel(ActArgs a) {
   }
 }
 
-__global__ void calib_finalize_kernel(float *act, int n) {
+// DualScale: s+ = max/127, s- = |min|/128.  Single scale (one symmetric
+// range per segment): s = max(max, |min|)/127 in both halves, so that the
+// dual-scale quantiser then produces the plain symmetric codes in
+// [-127, 127].
+__global__ void calib_finalize_kernel(float *act, int n, int single) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   float mx = act[i], mn = act[n + i];
   float sp, ip, sn, in;
-  scale_pair(mx, 127.0, sp, ip);
-  scale_pair(mn, 128.0, sn, in);
+  if (single) {
+    scale_pair(fmaxf(mx, mn), 127.0, sp, ip);
+    sn = sp;
+    in = ip;
+  } else {
+    scale_pair(mx, 127.0, sp, ip);
+    scale_pair(mn, 128.0, sn, in);
+  }
   act[i] = sp;
   act[n + i] = sn;
   act[2 * n + i] = ip;
@@ -103,7 +119,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(ActArgs a) {
   const int seg = blockIdx.y;
   const int64_t k0 = a.ks.off[seg], k1 = a.ks.end[seg];
   const float inv_pos = a.act[2 * a.n_kseg + seg];
-  const float inv_neg = a.act[3 * a.n_kseg + seg];
+  const float inv_neg = a.single ? inv_pos : a.act[3 * a.n_kseg + seg];
   const int L = 1 << a.lanes_log2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane >> a.lanes_log2, col = lane & (L - 1);
@@ -157,7 +173,7 @@ void plan_rows(int64_t M, const SegTable &ks, ActArgs &a) {
 }  // namespace
 
 hipError_t launch_calibrate(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
-                            const SegTable &ks, float *act, hipStream_t s) {
+                            const SegTable &ks, float *act, bool single, hipStream_t s) {
   const int n = ks.n;
   hipLaunchKernelGGL(calib_init_kernel, dim3((2 * n + 255) / 256), dim3(256), 0, s, act, n);
   if (M > 0) {
@@ -167,15 +183,17 @@ hipError_t launch_calibrate(const uint16_t *x, int64_t M, int64_t K, int64_t ld_
     dim3 grid((unsigned)((M + a.rows_per_block - 1) / a.rows_per_block), (unsigned)n);
     hipLaunchKernelGGL(calib_reduce_kernel, grid, dim3(256), 0, s, a);
   }
-  hipLaunchKernelGGL(calib_finalize_kernel, dim3((n + 255) / 256), dim3(256), 0, s, act, n);
+  hipLaunchKernelGGL(calib_finalize_kernel, dim3((n + 255) / 256), dim3(256), 0, s, act, n,
+                     single ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
                            const SegTable &ks, const float *act, int8_t *q, int64_t ld_q,
-                           int32_t layout, hipStream_t s) {
+                           int32_t layout, bool single, hipStream_t s) {
   if (M == 0) return hipSuccess;
   ActArgs a{};
+  a.single = single ? 1 : 0;
   a.x = x; a.M = M; a.K = K; a.ld_x = ld_x; a.act = act; a.q = q; a.ld_q = ld_q;
   a.n_kseg = ks.n; a.ks = ks;
   a.plane_stride = layout ? M * ld_q : 0;

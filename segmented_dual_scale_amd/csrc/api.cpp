@@ -131,16 +131,29 @@ size_t segquant_weight_packed_bytes(int64_t K, int64_t N) {
   return (size_t)K * (size_t)N;
 }
 
-int segquant_calibrate_amax(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ld_x,
-                            int32_t n_kseg, const int32_t *kseg_offset,
-                            const int32_t *kseg_width, float *act_scales, void *stream) {
+static int calibrate(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ld_x, int32_t n_kseg,
+                     const int32_t *kseg_offset, const int32_t *kseg_width, float *act_scales,
+                     bool single, void *stream) {
   int st = check_x(x_bf16, M, K, ld_x);
   if (st) return st;
   if (!act_scales) return fail(SEGQ_ERR_NULL, "act_scales is NULL");
   sq::SegTable ks{};
   if ((st = read_kseg(n_kseg, kseg_offset, kseg_width, K, 0, ks))) return st;
-  return hip_status(sq::launch_calibrate(x_bf16, M, K, ld_x, ks, act_scales, (hipStream_t)stream),
-                    "calibrate launch");
+  return hip_status(
+      sq::launch_calibrate(x_bf16, M, K, ld_x, ks, act_scales, single, (hipStream_t)stream),
+      "calibrate launch");
+}
+
+int segquant_calibrate_amax(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ld_x,
+                            int32_t n_kseg, const int32_t *kseg_offset,
+                            const int32_t *kseg_width, float *act_scales, void *stream) {
+  return calibrate(x_bf16, M, K, ld_x, n_kseg, kseg_offset, kseg_width, act_scales, false, stream);
+}
+
+int segquant_calibrate_amax_single(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ld_x,
+                                   int32_t n_kseg, const int32_t *kseg_offset,
+                                   const int32_t *kseg_width, float *act_scales, void *stream) {
+  return calibrate(x_bf16, M, K, ld_x, n_kseg, kseg_offset, kseg_width, act_scales, true, stream);
 }
 
 int segquant_quantize_dualscale(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ld_x,
@@ -159,7 +172,7 @@ int segquant_quantize_dualscale(const uint16_t *x_bf16, int64_t M, int64_t K, in
   sq::SegTable ks{};
   if ((st = read_kseg(n_kseg, kseg_offset, kseg_width, K, 0, ks))) return st;
   return hip_status(sq::launch_quantize(x_bf16, M, K, ld_x, ks, act_scales, q_out, ld_q, q_layout,
-                                        (hipStream_t)stream),
+                                        false, (hipStream_t)stream),
                     "quantize launch");
 }
 
@@ -210,7 +223,8 @@ static int gemm_check(int64_t M, int64_t N, int64_t K, uint32_t flags) {
   if (K % 64 || N % 16)
     return fail(SEGQ_ERR_ALIGN, "GEMM needs K %% 64 == 0 and N %% 16 == 0 (K=%lld N=%lld)",
                 (long long)K, (long long)N);
-  if (flags & ~(SEGQ_GEMM_FORCE_TILE | SEGQ_GEMM_FORCE_SMALLM | SEGQ_GEMM_FUSED_QUANT))
+  if (flags & ~(SEGQ_GEMM_FORCE_TILE | SEGQ_GEMM_FORCE_SMALLM | SEGQ_GEMM_FUSED_QUANT |
+                SEGQ_GEMM_SINGLE_SCALE))
     return fail(SEGQ_ERR_SHAPE, "unknown flags 0x%x", flags);
   if ((flags & SEGQ_GEMM_FORCE_TILE) && (flags & SEGQ_GEMM_FORCE_SMALLM))
     return fail(SEGQ_ERR_SHAPE, "both kernels forced");
@@ -264,6 +278,8 @@ int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
     } else {
       if (q_layout != SEGQ_Q_SIGNED && q_layout != SEGQ_Q_PLANES)
         return fail(SEGQ_ERR_SHAPE, "unknown q_layout %d", q_layout);
+      if (q_layout == SEGQ_Q_PLANES && (flags & SEGQ_GEMM_SINGLE_SCALE))
+        return fail(SEGQ_ERR_UNSUPPORTED, "the single-scale product takes bf16 or signed-code input");
       if (ld_q < K) return fail(SEGQ_ERR_SHAPE, "ld_q %lld < K %lld", (long long)ld_q, (long long)K);
       if (ld_q % 16 != 0)
         return fail(SEGQ_ERR_ALIGN, "ld_q %lld is not a multiple of 16", (long long)ld_q);
@@ -293,13 +309,14 @@ int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
   p.w_packed = w_packed; p.w_scale = w_scale; p.act = act_scales;
   p.ks = ks;
   p.y = y_bf16; p.ld_y = ld_y; p.acc_debug = acc_debug;
+  p.single_scale = (flags & SEGQ_GEMM_SINGLE_SCALE) != 0;
   const int kernel = segquant_gemm_kernel_for(M, N, K, flags);
   if (x_bf16 && workspace && quantize_first(kernel, M, N, ks, flags) &&
       workspace_bytes >= (size_t)(M * K)) {
     // quantise once into the workspace, then the GEMM from the signed codes
     int8_t *codes = static_cast<int8_t *>(workspace);
     hipError_t e = sq::launch_quantize(x_bf16, M, K, ld_x, ks, act_scales, codes, K,
-                                       SEGQ_Q_SIGNED, (hipStream_t)stream);
+                                       SEGQ_Q_SIGNED, p.single_scale, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "quantize launch");
     p.x = nullptr;
     p.ld_x = 0;

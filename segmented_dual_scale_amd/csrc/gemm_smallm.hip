@@ -57,6 +57,7 @@ struct SmallArgs {
   int64_t ld_y;
   int32_t *acc;
   int32_t n_kseg;
+  int32_t single;  // single scale: the + half's scales for both signs, one dumped product
   int32_t seg_end_tile[kMaxKSeg];
 };
 
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(64 * WPG) void gemm_smallm_chunked_kernel(SmallArgs
   uint8_t *plane_p = xs;
   uint8_t *plane_n = xs + a.M * pitch;
   const int nS = a.n_kseg;
-  const float *s_pos = a.act, *s_neg = a.act + nS;
+  const float *s_pos = a.act, *s_neg = a.act + (a.single ? 0 : nS);
 
   // thread -> (row, first 16-byte piece) for staging X: threads per row is a
   // power of two
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(64 * WPG) void gemm_smallm_chunked_kernel(SmallArgs
     // do not wait behind the vector loads above)
     if (ONE || kc0 == 0) {
       for (int i = 0; i < nS; ++i) {
-        const float ip = a.act[2 * nS + i], in = a.act[3 * nS + i];
+        const float ip = a.act[2 * nS + i], in = a.act[(a.single ? 2 : 3) * nS + i];
         if (tid == (i & (NTHR - 1))) {
           inv_tab[2 * i] = ip;
           inv_tab[2 * i + 1] = in;
@@ -200,8 +201,12 @@ __global__ __launch_bounds__(64 * WPG) void gemm_smallm_chunked_kernel(SmallArgs
                 const int m = (lane >> 4) * 4 + r;
                 if (active && m < a.M) {
                   const int64_t o = ((int64_t)seg * a.M + m) * a.N + n;
-                  a.acc[o] = accp[r];
-                  a.acc[(int64_t)nS * a.M * a.N + o] = accn[r];
+                  if (a.single) {
+                    a.acc[o] = accp[r] + accn[r];
+                  } else {
+                    a.acc[o] = accp[r];
+                    a.acc[(int64_t)nS * a.M * a.N + o] = accn[r];
+                  }
                 }
               }
             }
@@ -263,6 +268,7 @@ struct StreamArgs {
   int32_t *acc;
   int32_t n_kseg;      // <= kStreamMaxKT (every segment is whole k-tiles)
   uint32_t fold_mask;  // bit t: a K-segment ends with k-tile t
+  int32_t single;      // single scale: the + half's scales for both signs, one dumped product
 };
 
 // QL: activation input, -1 bf16 (quantised here), 0 signed codes, 1 planes.
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
     if (QL < 0) {
       const int sg = __builtin_popcount(a.fold_mask & ((1u << (c >> 3)) - 1u));
       ipv[QL < 0 ? i : 0] = a.act[2 * nS + sg];
-      inv_[QL < 0 ? i : 0] = a.act[3 * nS + sg];
+      inv_[QL < 0 ? i : 0] = a.act[(a.single ? 2 : 3) * nS + sg];
     }
   }
 
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   //     column n (a queue: each fold takes the head and fetches one more)
   const int ti = min(lane & 31, nS - 1);
   const float sp_l = a.act[ti];
-  const float sn_l = a.act[nS + ti];
+  const float sn_l = a.act[(a.single ? 0 : nS) + ti];
   float wsp[kStreamPre];
 #pragma unroll
   for (int j = 0; j < kStreamPre; ++j) wsp[j] = a.w_scale[(int64_t)min(j, nS - 1) * a.N + n];
@@ -430,8 +436,9 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = (lane >> 4) * 2 + (r & 1);
-        if (active && m < a.M)
-          a.acc[((int64_t)((r >> 1) * nS + seg) * a.M + m) * a.N + n] = C[r];
+        if (active && m < a.M && !(a.single && r >= 2))
+          a.acc[((int64_t)((r >> 1) * nS + seg) * a.M + m) * a.N + n] =
+              a.single ? C[r] + C[(r + 2) & 3] : C[r];
       }
     }
     const float ws = next_wscale(seg);
@@ -449,8 +456,12 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
         const int m = (lane >> 4) * 4 + r;
         if (active && m < a.M) {
           const int64_t o = ((int64_t)seg * a.M + m) * a.N + n;
-          a.acc[o] = P[r];
-          a.acc[(int64_t)nS * a.M * a.N + o] = Q[r];
+          if (a.single) {
+            a.acc[o] = P[r] + Q[r];
+          } else {
+            a.acc[o] = P[r];
+            a.acc[(int64_t)nS * a.M * a.N + o] = Q[r];
+          }
         }
       }
     }
@@ -581,6 +592,7 @@ hipError_t launch_stream(const GemmProblem &p, hipStream_t s) {
   a.y = p.y;
   a.ld_y = p.ld_y;
   a.acc = p.acc_debug;
+  a.single = p.single_scale ? 1 : 0;
   a.n_kseg = p.ks.n;
   a.fold_mask = 0;
   for (int i = 0; i < p.ks.n; ++i) a.fold_mask |= 1u << (p.ks.end[i] / 64 - 1);
@@ -628,6 +640,7 @@ hipError_t launch_gemm_smallm(const GemmProblem &p, hipStream_t s) {
   a.y = p.y;
   a.ld_y = p.ld_y;
   a.acc = p.acc_debug;
+  a.single = p.single_scale ? 1 : 0;
   a.n_kseg = p.ks.n;
   for (int i = 0; i < p.ks.n; ++i) a.seg_end_tile[i] = p.ks.end[i] / 64;
   dim3 grid((unsigned)((p.N / 16 + WPG - 1) / WPG)), block(NTHR);

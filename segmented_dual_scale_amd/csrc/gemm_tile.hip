@@ -68,7 +68,10 @@ namespace {
 constexpr int kAPitch = 144;  // bytes per LDS row of one A plane (128 + 16 pad)
 constexpr int kBK = 128;      // K per LDS stage
 
-enum AMode { A_BF16 = 0, A_SIGNED = 1, A_PLANES = 2 };
+// Activation input: bf16 (quantised here), signed codes, two planes; and the
+// single-scale forms of the first two (one product on the signed code, the
+// + half's scales for both signs).
+enum AMode { A_BF16 = 0, A_SIGNED = 1, A_PLANES = 2, A_BF16_1 = 3, A_SIGNED_1 = 4 };
 // MULTI folds at stage ends (every segment end but the last on a multiple of
 // 128); MULTI64 checks after every 64-wide k-step.
 enum Mode { SINGLE = 0, STEP = 1, MULTI = 2, MULTI64 = 3 };
@@ -111,7 +114,9 @@ constexpr int pieces_in_sub(int xp, int ks) {
 // in sub-block 3 (after the barrier; its buffer was last read in stage u - 1).
 // Each sub-block then carries one piece's vector ALU work beside its twelve
 // matrix-core instructions instead of two, one, one and none.
-constexpr bool spread_quant(int mode, int amode, int xp) { return mode == 0 && amode == 0 && xp == 4; }
+constexpr bool spread_quant(int mode, int amode, int xp) {
+  return mode == 0 && (amode == 0 || amode == 3) && xp == 4;
+}
 
 // Segment end i, read straight from the kernel-argument segment (the
 // argument is the only one, at offset 0).  Indexing the by-value argument
@@ -128,13 +133,15 @@ __device__ __forceinline__ v16i mfma32(const v4u &a, const v4u &b, const v16i &c
 }
 
 template <int BM, int BN, int AMODE, int MODE, bool DEBUG>
-__global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) void gemm_tile_kernel(TileArgs a) {
+__global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16 && AMODE != A_BF16_1) ? 2 : 1) void gemm_tile_kernel(TileArgs a) {
   constexpr int WN = BN / 4;   // columns per wave
   constexpr int MB = BM / 32;  // 32-row blocks
   constexpr int NB = WN / 32;  // 32-column blocks per wave
   constexpr int A_PLANE = BM * kAPitch, A_STAGE = 2 * A_PLANE;
   // 16-byte activation pieces per thread per stage
-  constexpr int XP = AMODE == A_SIGNED ? BM / 32 : BM / 16;
+  constexpr bool IN_BF16 = AMODE == A_BF16 || AMODE == A_BF16_1;
+  constexpr bool ONE = AMODE == A_BF16_1 || AMODE == A_SIGNED_1;  // single scale
+  constexpr int XP = (AMODE == A_SIGNED || AMODE == A_SIGNED_1) ? BM / 32 : BM / 16;
   static_assert(BM % 32 == 0 && WN % 32 == 0, "tile sizes");
 
   // three stage buffers of quantised planes: stage u is read from buffer
@@ -204,8 +211,8 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
   // A thread's pieces lie in one 64-wide half of the stage (k-tile 2u or
   // 2u+1); a half past K loads the last k-tile instead (in bounds) and
   // stores zero codes.
-  const int my_half = AMODE == A_BF16 ? (tid & 15) >> 3 : (tid & 7) >> 2;
-  const int half_off = AMODE == A_BF16 ? (tid & 7) * 8 : (tid & 3) * 16;  // elements
+  const int my_half = IN_BF16 ? (tid & 15) >> 3 : (tid & 7) >> 2;
+  const int half_off = IN_BF16 ? (tid & 7) * 8 : (tid & 3) * 16;  // elements
   // XS register slots: stage v's pieces go to slot v % XS, loaded at the
   // start of stage v - XS and quantised during stage v - 1 (XS - 1 stages of
   // memory latency hidden).  Three for the single-segment loop; the fold
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const uint8_t *p;
-      if (AMODE == A_BF16) {
+      if (IN_BF16) {
         const int m = min(m0 + i * 16 + (tid >> 4), a.M - 1);  // rows past M: any valid row
         p = reinterpret_cast<const uint8_t *>(a.x) + ((int64_t)m * a.ld_x + col) * 2;
       } else {
@@ -242,7 +249,13 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
     v4u xv = xr[s][i];
 #pragma unroll
     for (int e = 0; e < 4; ++e) xv[e] = valid ? xv[e] : 0u;
-    if (AMODE == A_BF16) {
+    if (AMODE == A_BF16_1) {  // one plane of signed codes, the + half's inverse for both signs
+      const int off = (i * 16 + (tid >> 4)) * kAPitch + (tid & 15) * 8;
+      *reinterpret_cast<v2u *>(ap + off) = quant8_signed(xv, inv_pos, inv_pos);
+    } else if (AMODE == A_SIGNED_1) {
+      const int off = (i * 32 + (tid >> 3)) * kAPitch + (tid & 7) * 16;
+      *reinterpret_cast<v4u *>(ap + off) = xv;
+    } else if (AMODE == A_BF16) {
       const int off = (i * 16 + (tid >> 4)) * kAPitch + (tid & 15) * 8;
       v2u p, n;
       quant8_planes(xv, inv_pos, inv_neg, p, n);
@@ -275,7 +288,7 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       fa[f][mb] = *reinterpret_cast<const v4u *>(buf + arow + mb * 32 * kAPitch + ks * 32);
-      fb[f][mb] = *reinterpret_cast<const v4u *>(buf + A_PLANE + arow + mb * 32 * kAPitch + ks * 32);
+      if (!ONE) fb[f][mb] = *reinterpret_cast<const v4u *>(buf + A_PLANE + arow + mb * 32 * kAPitch + ks * 32);
     }
   };
 
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
       if (m >= a.M) continue;
       const int64_t o = ((int64_t)seg * a.M + m) * a.N + col;
       a.acc[o] = p[r];
-      a.acc[(int64_t)nS * a.M * a.N + o] = n[r];
+      if (!ONE) a.acc[(int64_t)nS * a.M * a.N + o] = n[r];
     }
   };
 
@@ -373,8 +386,10 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
         if (DEBUG && t < KT) dump(t, mb, nb, accp[mb][nb], accn[mb][nb]);
         v16f &yv = yacc[YREG ? mb : 0][YREG ? nb : 0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)  // element by element: few temporaries
-          yv[r] = __builtin_fmaf(cn, (float)accn[mb][nb][r], __builtin_fmaf(cp, (float)accp[mb][nb][r], yv[r]));
+        for (int r = 0; r < 16; ++r) {  // element by element: few temporaries
+          const float t = __builtin_fmaf(cp, (float)accp[mb][nb][r], yv[r]);
+          yv[r] = ONE ? t : __builtin_fmaf(cn, (float)accn[mb][nb][r], t);
+        }
       }
     }
   };
@@ -395,8 +410,10 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
         if (DEBUG) dump(seg, mb, nb, accp[mb][nb], accn[mb][nb]);
         v16f &yv = yacc[YREG ? mb : 0][YREG ? nb : 0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          yv[r] = __builtin_fmaf(cn, (float)accn[mb][nb][r], __builtin_fmaf(cp, (float)accp[mb][nb][r], yv[r]));
+        for (int r = 0; r < 16; ++r) {
+          const float t = __builtin_fmaf(cp, (float)accp[mb][nb][r], yv[r]);
+          yv[r] = ONE ? t : __builtin_fmaf(cn, (float)accn[mb][nb][r], t);
+        }
       }
       wsa[nb] = wsb[nb];
       wsb[nb] = col_ws(seg + 2, nb);
@@ -508,10 +525,10 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
           const v4u &xb = (ks & 1) ? fb[1][mb] : fb[0][mb];
           if (MODE == STEP && (ks & 1) == 0) {  // a k-step's products start from 0
             accp[mb][nb] = mfma32(xa, wr[s][nb][ks], v16i{});
-            accn[mb][nb] = mfma32(xb, wr[s][nb][ks], v16i{});
+            if (!ONE) accn[mb][nb] = mfma32(xb, wr[s][nb][ks], v16i{});
           } else {
             accp[mb][nb] = mfma32(xa, wr[s][nb][ks], accp[mb][nb]);
-            accn[mb][nb] = mfma32(xb, wr[s][nb][ks], accn[mb][nb]);
+            if (!ONE) accn[mb][nb] = mfma32(xb, wr[s][nb][ks], accn[mb][nb]);
           }
         }
         load_w1(ic<s>{}, nb, ks, u + 2);  // refill with the stage two ahead
@@ -535,10 +552,10 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
         // vector ALU work (quantisation), the weight refills spread among
         // them, the LDS writes last.  Without it the ALU work comes in
         // clumps of ~100 instructions during which the matrix cores idle.
-        constexpr int NMF = 2 * MB * NB;
+        constexpr int NMF = (ONE ? 1 : 2) * MB * NB;
         constexpr int nq = SPREAD ? 1 : pieces_in_sub(XP, ks);
-        constexpr int vpq = AMODE == A_BF16 ? 56 : AMODE == A_SIGNED ? 16 : 0;
-        constexpr int vfold = (MODE == STEP && (ks & 1)) ? MB * NB * 16 * 4 : 0;
+        constexpr int vpq = AMODE == A_BF16 ? 56 : AMODE == A_BF16_1 ? 38 : AMODE == A_SIGNED ? 16 : 0;
+        constexpr int vfold = (MODE == STEP && (ks & 1)) ? MB * NB * 16 * (ONE ? 2 : 4) : 0;
         constexpr int per = (nq * vpq + vfold + NMF - 1) / NMF + 1;
 #pragma unroll
         for (int j = 0; j < NMF; ++j) {
@@ -625,8 +642,12 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
       v16f v;
       if (MODE == SINGLE) {
         const v16f P = __builtin_convertvector(accp[mb][nb], v16f);
-        const v16f Q = __builtin_convertvector(accn[mb][nb], v16f);
-        v = __builtin_elementwise_fma(v16f(cn), Q, v16f(cp) * P);
+        if (ONE) {
+          v = v16f(cp) * P;
+        } else {
+          const v16f Q = __builtin_convertvector(accn[mb][nb], v16f);
+          v = __builtin_elementwise_fma(v16f(cn), Q, v16f(cp) * P);
+        }
       } else {
         v = yacc[YREG ? mb : 0][YREG ? nb : 0];
       }
@@ -641,9 +662,11 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16) ? 2 : 1) voi
 
 // The accumulator dump of a multi-segment launch holds running sums S_i;
 // turn them into per-segment sums A_i = S_i - S_{i-1} (exact in int32).
-__global__ __launch_bounds__(256) void acc_difference_kernel(int32_t *acc, int n_kseg, int64_t mn) {
+// (planes: 2, or 1 when only the single-scale product was dumped)
+__global__ __launch_bounds__(256) void acc_difference_kernel(int32_t *acc, int n_kseg, int64_t mn,
+                                                             int planes) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= 2 * mn) return;
+  if (e >= planes * mn) return;
   const int64_t h = e / mn, o = e - h * mn;
   int32_t *base = acc + h * n_kseg * mn + o;
   for (int seg = n_kseg - 1; seg >= 1; --seg) base[seg * mn] -= base[(seg - 1) * mn];
@@ -659,11 +682,15 @@ hipError_t launch_variant(TileArgs t, int amode, bool debug, hipStream_t s) {
   if (debug) {
     if (amode == A_BF16) SQ_LAUNCH(A_BF16, true);
     else if (amode == A_SIGNED) SQ_LAUNCH(A_SIGNED, true);
-    else SQ_LAUNCH(A_PLANES, true);
+    else if (amode == A_PLANES) SQ_LAUNCH(A_PLANES, true);
+    else if (amode == A_BF16_1) SQ_LAUNCH(A_BF16_1, true);
+    else SQ_LAUNCH(A_SIGNED_1, true);
   } else {
     if (amode == A_BF16) SQ_LAUNCH(A_BF16, false);
     else if (amode == A_SIGNED) SQ_LAUNCH(A_SIGNED, false);
-    else SQ_LAUNCH(A_PLANES, false);
+    else if (amode == A_PLANES) SQ_LAUNCH(A_PLANES, false);
+    else if (amode == A_BF16_1) SQ_LAUNCH(A_BF16_1, false);
+    else SQ_LAUNCH(A_SIGNED_1, false);
   }
 #undef SQ_LAUNCH
   return hipGetLastError();
@@ -693,7 +720,8 @@ hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s) {
     t.seg_end_tile[i] = p.ks.end[i] / 64;
     every_step = every_step && (p.ks.end[i] - p.ks.off[i] == 64);
   }
-  const int amode = p.x ? A_BF16 : (p.q_layout == 1 ? A_PLANES : A_SIGNED);
+  const int amode = p.single_scale ? (p.x ? A_BF16_1 : A_SIGNED_1)
+                                   : p.x ? A_BF16 : (p.q_layout == 1 ? A_PLANES : A_SIGNED);
   const bool debug = p.acc_debug != nullptr;
   // (the tile widths here and in tile_columns() go together)
   if (p.ks.n == 1) return launch_variant<64, 384, SINGLE>(t, amode, debug, s);
@@ -704,8 +732,9 @@ hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s) {
                            : launch_variant<64, 256, MULTI64>(t, amode, debug, s);
   if (e != hipSuccess || !debug) return e;
   const int64_t mn = p.M * p.N;
-  hipLaunchKernelGGL(acc_difference_kernel, dim3((unsigned)((2 * mn + 255) / 256)), dim3(256), 0, s,
-                     p.acc_debug, p.ks.n, mn);
+  const int planes = p.single_scale ? 1 : 2;
+  hipLaunchKernelGGL(acc_difference_kernel, dim3((unsigned)((planes * mn + 255) / 256)), dim3(256),
+                     0, s, p.acc_debug, p.ks.n, mn, planes);
   return hipGetLastError();
 }
 

@@ -23,12 +23,14 @@ struct NSegTable {
   int32_t end[kMaxNSeg];
 };
 
+// single: one symmetric scale per segment, written into both halves
 hipError_t launch_calibrate(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
-                            const SegTable &ks, float *act, hipStream_t s);
+                            const SegTable &ks, float *act, bool single, hipStream_t s);
 
+// single: both signs quantised with the + half's inverse
 hipError_t launch_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
                            const SegTable &ks, const float *act, int8_t *q, int64_t ld_q,
-                           int32_t layout, hipStream_t s);
+                           int32_t layout, bool single, hipStream_t s);
 
 hipError_t launch_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w,
                                   const SegTable &ks, const NSegTable &ns, bool per_column,
@@ -51,6 +53,7 @@ struct GemmProblem {
   uint16_t *y;
   int64_t ld_y;
   int32_t *acc_debug;
+  bool single_scale;  // one product on the signed code, + half's scales only
 };
 
 hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s);

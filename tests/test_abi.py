@@ -128,7 +128,8 @@ def gemm(M=64, N=64, K=128, x=FAKE, ld_x=None, xq=None, ld_q=0, q_layout=0, w=FA
     (dict(K=132160, widths=[66048, 66112]), S.SEGQ_ERR_UNSUPPORTED),  # running sums over all of K
     (dict(M=17, flags=S.SEGQ_GEMM_FORCE_SMALLM), S.SEGQ_ERR_UNSUPPORTED),
     (dict(flags=3), S.SEGQ_ERR_SHAPE),
-    (dict(flags=8), S.SEGQ_ERR_SHAPE),
+    (dict(flags=16), S.SEGQ_ERR_SHAPE),
+    (dict(x=None, xq=FAKE, ld_q=128, q_layout=1, flags=8), S.SEGQ_ERR_UNSUPPORTED),
 ])
 def test_gemm_validation(kwargs, status):
     assert gemm(**kwargs) == status

@@ -203,6 +203,59 @@ def test_gemm_quantize_first_parity(M, K, N, kseg):
         assert ok, f"fused Y out of tolerance: {nbad} elements, worst excess {worst}"
 
 
+# ------------------------------------------------- single-scale mode ----
+SINGLE_CASES = [
+    # M, K, N, kseg, kind
+    (2, 1536, 576, [1536], "silu"),            # streaming small-M kernel, both halves in one operand
+    (12, 640, 256, [64] * 10, "blocks"),       # streaming small-M kernel, ten segments
+    (333, 512, 320, [512], "gelu"),            # tile kernel, one segment
+    (77, 384, 768, [128, 256], "gelu"),        # tile kernel, segments ending on whole stages
+    (130, 704, 64, [64, 128, 512], "normal"),  # tile kernel, a segment ending inside a stage
+    (200, 1536, 1536, [64] * 24, "blocks"),    # tile kernel, one k-step per segment; quantise-first
+    (300, 512, 2304, [512], "gelu"),           # tile kernel, one segment, quantise-first
+]
+
+
+@pytest.mark.parametrize("case", SINGLE_CASES, ids=[f"M{c[0]}_K{c[1]}_N{c[2]}_S{len(c[3])}" for c in SINGLE_CASES])
+@pytest.mark.parametrize("mode", ["bf16", "signed"])
+def test_single_scale_parity(case, mode):
+    """Single-scale W8A8 (SEGQ_GEMM_SINGLE_SCALE with the single-scale
+    table): table bit-exact; the one product per segment (dumped in plane 0)
+    equals the oracle's A+ + A- bit-exact; plane 1 untouched; Y within
+    tolerance, with and without the dump."""
+    import torch
+    M, K, N, kseg, kind = case
+    x, w = W.make_custom(M, K, N, seed=M + K + N, kind=kind, x_scale=2.0)
+    s, s2, inv, inv2 = oracle.calibrate_amax_single(x, kseg)
+    wq, ws = oracle.quantize_weight(w, kseg, None, True)
+    qp, qn = oracle.quantize_dualscale(x, kseg, inv, inv2)
+    acc_ref = oracle.segment_acc(qp, qn, wq, kseg)
+    y_ref = oracle.dequantize(acc_ref, s, s2, ws)
+    xd = to_dev_bf16(x)
+    act = S.segquant_calibrate_amax_single(xd, kseg)
+    ref_tab = np.stack([s, s2, inv, inv2])
+    assert np.array_equal(act.cpu().numpy().view(np.uint32), ref_tab.view(np.uint32))
+    wp, gws = S.segquant_quantize_weight(to_dev(w), kseg, None, True)
+    xq = S.segquant_quantize_dualscale(xd, act, kseg, S.SEGQ_Q_SIGNED) if mode == "signed" else None
+    for debug in (True, False):
+        acc = (torch.full((2, len(kseg), M, N), -7, dtype=torch.int32, device=DEV)
+               if debug else None)
+        if mode == "bf16":
+            y = S.segquant_gemm_w8a8_seg(xd, wp, gws, act, kseg, acc_debug=acc,
+                                         flags=S.SEGQ_GEMM_SINGLE_SCALE)
+        else:
+            y = S.segquant_gemm_w8a8_seg(None, wp, gws, act, kseg, N=N, xq=xq,
+                                         q_layout=S.SEGQ_Q_SIGNED, acc_debug=acc,
+                                         flags=S.SEGQ_GEMM_SINGLE_SCALE)
+        torch.cuda.synchronize()
+        if debug:
+            a = acc.cpu().numpy()
+            assert np.array_equal(a[0], acc_ref[0] + acc_ref[1]), "single-scale product differs"
+            assert np.all(a[1] == -7), "plane 1 was written"
+        ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), y_ref)
+        assert ok, f"single-scale Y out of tolerance (debug={debug}): {nbad} elements, worst {worst}"
+
+
 def test_gemm_empty_batch_is_a_noop():
     import torch
     x, w = W.make_custom(4, 128, 32, seed=3)

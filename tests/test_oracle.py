@@ -347,6 +347,68 @@ def test_dualscale_beats_single_scale_on_skewed_input():
     assert e_dual < 0.2 * e_single
 
 
+# --------------------------------------------------- single-scale mode ----
+@pytest.mark.parametrize("kind", ["gelu", "silu", "blocks", "neg"])
+def test_single_scale_calibration(kind):
+    """The single-scale baseline [P2 deployment-cost table, INT8 baseline;
+    P1 limitations, DualScale per layer]: per segment the element of largest
+    magnitude maps to exactly +-127, every code lies in [-127, 127], and
+    negating X negates every code under the same table (one symmetric
+    step, unlike the two-scale table)."""
+    kseg = [64, 192]
+    x, _ = W.make_custom(24, 256, 8, seed=23, kind=kind, x_scale=2.5)
+    s, s2, inv, inv2 = oracle.calibrate_amax_single(x, kseg)
+    assert np.array_equal(s, s2) and np.array_equal(inv, inv2)
+    qp, qn = oracle.quantize_dualscale(x, kseg, inv, inv2)
+    q = qp.astype(np.int32) + qn
+    assert q.min() >= -127 and q.max() <= 127
+    xf = fl(x)
+    for i, (lo, hi) in enumerate([(0, 64), (64, 256)]):
+        seg = np.abs(xf[:, lo:hi])
+        r, c = np.unravel_index(np.argmax(seg), seg.shape)
+        assert abs(q[r, lo + c]) == 127
+    xneg = bits(-xf)
+    s_n, _, inv_n, _ = oracle.calibrate_amax_single(xneg, kseg)
+    assert np.array_equal(s_n, s) and np.array_equal(inv_n, inv)
+    qpn, qnn = oracle.quantize_dualscale(xneg, kseg, inv_n, inv_n)
+    assert np.array_equal(qpn.astype(np.int32) + qnn, -q)
+
+
+def test_single_scale_nonnegative_input_matches_dualscale_positive_half():
+    """On an all-nonnegative X the single range max|x| is max x, so the
+    single-scale table equals the DualScale table's + half."""
+    x, _ = W.make_custom(10, 128, 8, seed=29, kind="pos")
+    s, _, inv, _ = oracle.calibrate_amax_single(x, [128])
+    sp, _, ip, _ = oracle.calibrate_amax(x, [128])
+    assert np.array_equal(s, sp) and np.array_equal(inv, ip)
+
+
+@pytest.mark.parametrize("kseg", [[256], [64, 64, 128]])
+def test_single_scale_layer_is_textbook_w8a8(kseg):
+    """With the single-scale table, the DualScale steps compute textbook
+    per-segment W8A8: codes q = clamp(rne(fp32(x * inv)), -127, 127) written
+    out here with numpy fp32 arithmetic, A_i = q_i W_q,i by an int64 numpy
+    matmul, y = sum_i s_i w_scale_i A_i."""
+    x, w = W.make_custom(16, 256, 24, seed=31, kind="gelu", x_scale=2.0)
+    s, s2, inv, inv2 = oracle.calibrate_amax_single(x, kseg)
+    wq, ws = oracle.quantize_weight(w, kseg, None, per_column=True)
+    qp, qn = oracle.quantize_dualscale(x, kseg, inv, inv2)
+    acc = oracle.segment_acc(qp, qn, wq, kseg)
+    y = oracle.dequantize(acc, s, s2, ws)
+    xf = fl(x)
+    edges = np.concatenate([[0], np.cumsum(kseg)])
+    yt = np.zeros((16, 24))
+    for i in range(len(kseg)):
+        lo, hi = edges[i], edges[i + 1]
+        prod = xf[:, lo:hi].astype(np.float32) * np.float32(inv[i])   # one fp32 multiply
+        q = np.clip(np.rint(prod), -127, 127).astype(np.int64)         # rint: half to even
+        assert np.array_equal(q, qp[:, lo:hi].astype(np.int64) + qn[:, lo:hi])
+        a = q @ wq[lo:hi].astype(np.int64)
+        assert np.array_equal(a, acc[0, i].astype(np.int64) + acc[1, i])
+        yt += float(s[i]) * a * ws[i].astype(np.float64)
+    np.testing.assert_allclose(y, yt, rtol=1e-12, atol=0)
+
+
 def test_composed_linear_equals_steps():
     x, w = W.make_custom(23, 256, 48, seed=19, kind="blocks")
     kseg = [64, 64, 128]
