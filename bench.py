@@ -156,13 +156,17 @@ class Layer:
         import numpy as np
         import torch
         self.S, self.mode = S, mode
+        # single: the single-scale W8A8 baseline (one symmetric scale per
+        # segment, one product), bf16 input
+        self.flags = S.SEGQ_GEMM_SINGLE_SCALE if mode == "single" else S.SEGQ_GEMM_AUTO
         wl, x, w = W.make_inputs(name)
         self.wl, self.x, self.w = wl, x, w
         self.kseg = list(wl.kseg)
         nseg = None if wl.per_column else list(wl.nseg)
         # offline: calibration + weight quantisation (not timed)
         xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-        self.act = S.segquant_calibrate_amax(xd, self.kseg)
+        self.act = (S.segquant_calibrate_amax_single(xd, self.kseg) if mode == "single"
+                    else S.segquant_calibrate_amax(xd, self.kseg))
         wd = torch.from_numpy(w).to(dev)
         wp, self.ws = S.segquant_quantize_weight(wd, self.kseg, nseg, wl.per_column)
         del wd
@@ -186,7 +190,7 @@ class Layer:
         self.kernel = "gemm_smallm_kernel" if kid == S.SEGQ_KERNEL_SMALLM else "gemm_tile_kernel"
         # the library's choice of quantising first (one workspace, reused by
         # every call, as a layer would)
-        nb = S.segquant_gemm_workspace_bytes(wl.M, wl.N, wl.K, self.kseg) \
+        nb = S.segquant_gemm_workspace_bytes(wl.M, wl.N, wl.K, self.kseg, self.flags) \
             if self.layout is None else 0
         self.work = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
         self.launches = 2 if nb else 1
@@ -197,10 +201,10 @@ class Layer:
         if self.gemm_only:
             S.segquant_gemm_w8a8_seg(None, self.wps[j], self.ws, self.act, self.kseg,
                                      N=self.wl.N, xq=self.work.view(self.wl.M, self.wl.K),
-                                     q_layout=S.SEGQ_Q_SIGNED, out=self.ys[j])
+                                     q_layout=S.SEGQ_Q_SIGNED, out=self.ys[j], flags=self.flags)
         elif self.layout is None:
             S.segquant_gemm_w8a8_seg(self.xs[j], self.wps[j], self.ws, self.act, self.kseg,
-                                     out=self.ys[j], workspace=self.work)
+                                     out=self.ys[j], workspace=self.work, flags=self.flags)
         else:
             S.segquant_gemm_w8a8_seg(None, self.wps[j], self.ws, self.act, self.kseg,
                                      N=self.wl.N, xq=self.xqs[j], q_layout=self.layout,
@@ -435,9 +439,10 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--mode", default="bf16", choices=["bf16", "signed", "planes"],
-                    help="bf16: fused quantisation (one launch); signed/planes: time the GEMM on "
-                         "an activation pre-quantised by segquant_quantize_dualscale")
+    ap.add_argument("--mode", default="bf16", choices=["bf16", "signed", "planes", "single"],
+                    help="bf16: the layer from bf16 input; signed/planes: time the GEMM on "
+                         "an activation pre-quantised by segquant_quantize_dualscale; single: the "
+                         "single-scale W8A8 baseline from bf16 input")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch each step from Python")
     ap.add_argument("--no-all", action="store_true", help="skip the all_workloads summary")
@@ -547,6 +552,15 @@ def main():
             lay.free()
             del lay
             torch.cuda.empty_cache()
+            if args.mode == "bf16":
+                # the single-scale baseline of the same layer: what DualScale costs
+                lay = Layer(S, W, dev, name, "single")
+                ms1, _ = lay.time(stream, 1, 10, use_graph, min_seconds=0.05)
+                summary[name]["single_scale_us_per_step"] = ms1 * 1e3
+                summary[name]["dualscale_over_single"] = ms / ms1
+                lay.free()
+                del lay
+                torch.cuda.empty_cache()
         line["all_workloads"] = summary
     if not args.no_peaks:
         mp = measured_peaks(dev, stream)
