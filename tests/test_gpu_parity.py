@@ -313,3 +313,48 @@ def test_full_size_workload(name):
         assert np.array_equal(acc_rows, ref.acc), f"{name} flags {flags}: int32 accumulators differ"
         ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(yd)[rows], ref.y, ymax)
         assert ok, f"{name} flags {flags}: accumulator-dumping variant out of tolerance, worst {worst}"
+
+
+# --------------------------------------- segments discovered from a graph ----
+def test_discovered_segments_drive_the_layer():
+    """The segment lists read off a module's graph (SegLinear discovery) go
+    straight into the layer: an attention output projection (K-segments per
+    head) and an AdaNorm projection (N-segments per modulation vector), each
+    run through the kernels and compared with the oracle on the same lists."""
+    import torch
+    from segmented_dual_scale_amd import seglinear
+
+    class AttnOut(torch.nn.Module):
+        def __init__(self):
+            super().__init__()
+            self.proj = torch.nn.Linear(4 * 64, 256)
+
+        def forward(self, o):
+            b, h, t, d = o.shape
+            return self.proj(o.transpose(1, 2).reshape(b, t, h * d))
+
+    class AdaNorm(torch.nn.Module):
+        def __init__(self):
+            super().__init__()
+            self.lin = torch.nn.Linear(256, 6 * 256)
+
+        def forward(self, e):
+            return self.lin(torch.nn.functional.silu(e)).chunk(6, dim=-1)
+
+    torch.manual_seed(0)
+    for mod, example, M in ((AttnOut(), torch.randn(1, 4, 3, 64), 150),
+                            (AdaNorm(), torch.randn(2, 256), 2)):
+        plan = next(iter(seglinear.discover(mod, example).values()))
+        assert plan.kernel_ready()
+        lin = mod.proj if isinstance(mod, AttnOut) else mod.lin
+        K, N = lin.in_features, lin.out_features
+        kseg = plan.kseg or [K]
+        nseg = plan.nseg or [N]
+        w = lin.weight.detach().t().contiguous().numpy().astype(np.float32)   # Y = X W, W [K][N]
+        x, _ = W.make_custom(M, K, 16, seed=M, kind="gelu", x_scale=2.0)
+        ref = OracleLayer(x, w, kseg, nseg, False)
+        gpu = GpuLayer(x, w, kseg, nseg, False)
+        y, acc = gpu.run("bf16", debug=True)
+        assert np.array_equal(acc.cpu().numpy(), ref.acc)
+        ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), ref.y)
+        assert ok, f"{type(mod).__name__}: {nbad} outputs out of tolerance, worst {worst}"
