@@ -360,6 +360,69 @@ def measured_peaks(dev, stream):
     return out
 
 
+def producer_fusion(S, W, dev, stream, names=("c2_adanorm_gemv", "c3_dit_ffn_fc2",
+                                                 "c5_flux_ffn_fc2")):
+    """The activation fused with the quantisation against the two passes it
+    replaces (activation to bf16 X in HBM, then quantisation), on the
+    pre-activations of the workloads whose X is SiLU/GELU output.  Codes as
+    signed int8; rotating copies of Z so the caches do not hold a step's
+    input."""
+    import numpy as np
+    import torch
+    out = {}
+    for name in names:
+        wl = W.WORKLOADS[name]
+        kind = W.preact_kind(wl)
+        act_kind = S.SEGQ_ACT_SILU if kind == "silu" else S.SEGQ_ACT_GELU
+        z0 = torch.from_numpy(W.make_preact(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+        kseg = list(wl.kseg)
+        _, x = S.segquant_activate_quantize(z0, act_kind, kseg=kseg, x_out=True, want_codes=False)
+        act = S.segquant_calibrate_amax(x, kseg)
+        elems = wl.M * wl.K
+        R = max(1, min(16, math.ceil(640e6 / (2 * elems))))
+        zs = [z0] + [z0.clone() for _ in range(R - 1)]
+        q = torch.empty((wl.M, wl.K), dtype=torch.int8, device=dev)
+
+        def fused(i):
+            S.segquant_activate_quantize(zs[i % R], act_kind, act, kseg, S.SEGQ_Q_SIGNED, out=q)
+
+        def unfused(i):
+            S.segquant_activate_quantize(zs[i % R], act_kind, kseg=kseg, x_out=x, want_codes=False)
+            S.segquant_quantize_dualscale(x, act, kseg, S.SEGQ_Q_SIGNED, out=q)
+
+        res = {}
+        for label, fn in (("fused", fused), ("unfused", unfused)):
+            with torch.cuda.stream(stream):
+                for i in range(2 * R):
+                    fn(i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(R):
+                    fn(i)
+            reps = max(1, math.ceil(40 / R))
+            with torch.cuda.stream(stream):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            res[label + "_us"] = e0.elapsed_time(e1) * 1e3 / (reps * R)
+            del g
+        res["activation"] = kind
+        res["elements"] = elems
+        res["fused_gbs"] = 3 * elems / (res["fused_us"] * 1e-6) / 1e9   # 2 B read, 1 B written
+        res["unfused_over_fused"] = res["unfused_us"] / res["fused_us"]
+        out[name] = res
+        del zs, x, q, z0
+        torch.cuda.empty_cache()
+    return out
+
+
 def copy_probe(dev, reps: int = 3):
     """A copy of known size (the scale of the FETCH_SIZE / WRITE_SIZE counters)."""
     import torch
@@ -446,6 +509,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch each step from Python")
     ap.add_argument("--no-all", action="store_true", help="skip the all_workloads summary")
+    ap.add_argument("--no-producer", action="store_true",
+                    help="skip the producer-fusion comparison (activation fused with quantisation)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured ceilings (matrix-core loop, streaming read)")
     ap.add_argument("--pmc-pass", action="store_true",
@@ -562,6 +627,8 @@ def main():
                 del lay
                 torch.cuda.empty_cache()
         line["all_workloads"] = summary
+    if not args.no_producer:
+        line["producer_fusion"] = producer_fusion(S, W, dev, stream)
     if not args.no_peaks:
         mp = measured_peaks(dev, stream)
         line["measured_peaks"] = mp

@@ -143,6 +143,36 @@ int segquant_quantize_dualscale(const uint16_t *x_bf16, int64_t M, int64_t K, in
                                 const int32_t *kseg_width, const float *act_scales,
                                 int8_t *q_out, int64_t ld_q, int32_t q_layout, void *stream);
 
+/* Activations for segquant_activate_quantize. */
+#define SEGQ_ACT_SILU 1 /* z / (1 + exp(-z)) */
+#define SEGQ_ACT_GELU 2 /* z/2 * (1 + erf(z / sqrt(2))), the exact form */
+
+/*
+ * segquant_activate_quantize -- the producer fused with the quantisation:
+ * the SiLU or GELU whose outputs carry the polarity asymmetry DualScale is
+ * for [P1 DualScale motivation; P2 section 3], applied to a bf16
+ * pre-activation and quantised in the same pass, so the activated bf16 X
+ * never round-trips through HBM.  Per element:
+ *   x = bf16_rne(act(z))   with act evaluated in fp32 (library expf;
+ *                          GELU as z/2 erfc(-z/sqrt 2), which is accurate
+ *                          for negative z)
+ *   codes of x exactly as segquant_quantize_dualscale
+ *   z_bf16      device bf16 [M][ld_z]
+ *   act_kind    SEGQ_ACT_SILU or SEGQ_ACT_GELU
+ *   act_scales  device fp32 [4][n_kseg], calibrated on x (may be NULL when
+ *               q_out is NULL)
+ *   q_out       optional device int8, layout and ld_q as for
+ *               segquant_quantize_dualscale
+ *   x_out       optional device bf16 [M][ld_xo]: x itself (for the offline
+ *               calibration, or for another consumer of the bf16 values)
+ * At least one of q_out and x_out.  One launch; M may be 0.
+ */
+int segquant_activate_quantize(const uint16_t *z_bf16, int64_t M, int64_t K, int64_t ld_z,
+                               int32_t act_kind, int32_t n_kseg, const int32_t *kseg_offset,
+                               const int32_t *kseg_width, const float *act_scales,
+                               int8_t *q_out, int64_t ld_q, int32_t q_layout, uint16_t *x_out,
+                               int64_t ld_xo, void *stream);
+
 /*
  * segquant_weight_packed_bytes -- size of the packed int8 weight for a
  * K x N layer: K*N bytes when K % 64 == 0 and N % 16 == 0, else 0.

@@ -55,12 +55,13 @@ def _load():
     lib.oracle_polarity_split.argtypes = [P, I64, P, P]
     lib.oracle_calibrate_amax.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, P]
     lib.oracle_calibrate_amax_single.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, P]
+    lib.oracle_activation.argtypes = [P, I64, I32, P]
     lib.oracle_quantize_dualscale.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, P]
     lib.oracle_quantize_weight.argtypes = [P, I64, I64, I64, I32, P, P, I32, P, P, I32, P, P]
     lib.oracle_segment_acc.argtypes = [P, P, P, I64, I64, I64, I32, P, P, P]
     lib.oracle_dequantize.argtypes = [P, I64, I64, I32, P, P, P, P]
     lib.oracle_dualscale_linear.argtypes = [P, I64, I64, I64, P, P, I64, I32, P, P, P, P, P, P, P]
-    for f in ("oracle_calibrate_amax", "oracle_calibrate_amax_single",
+    for f in ("oracle_calibrate_amax", "oracle_calibrate_amax_single", "oracle_activation",
               "oracle_quantize_dualscale", "oracle_quantize_weight",
               "oracle_segment_acc", "oracle_dequantize", "oracle_dualscale_linear"):
         getattr(lib, f).restype = ctypes.c_int
@@ -106,6 +107,15 @@ def calibrate_amax(x_bf16: np.ndarray, kseg: Sequence[int]):
     _check(_load().oracle_calibrate_amax(_ptr(x), M, K, K, len(wid), _ptr(off), _ptr(wid),
                                          *[_ptr(o) for o in out]), "calibrate_amax")
     return tuple(out)
+
+
+def activation(z_bf16: np.ndarray, kind: str) -> np.ndarray:
+    """SiLU ("silu") or exact GELU ("gelu") of bf16 values, in fp64."""
+    z = np.ascontiguousarray(z_bf16, dtype=np.uint16)
+    out = np.empty(z.shape, np.float64)
+    _check(_load().oracle_activation(_ptr(z), z.size, {"silu": 1, "gelu": 2}[kind], _ptr(out)),
+           "activation")
+    return out
 
 
 def calibrate_amax_single(x_bf16: np.ndarray, kseg: Sequence[int]):

@@ -134,6 +134,26 @@ int oracle_calibrate_amax(const uint16_t *x, int64_t M, int64_t K, int64_t ld,
 }
 
 /* ------------------------------------------------------------------------
+ * The producers of the activation [P1 DualScale motivation; P2 section 3:
+ * SiLU and GELU leave a wide positive and a narrow negative range], in fp64
+ * from a bf16 pre-activation z:
+ *   kind 1  SiLU  z / (1 + exp(-z))
+ *   kind 2  GELU  z/2 (1 + erf(z / sqrt 2))   (the exact form)
+ * The kernels evaluate these in fp32 and round to bf16; the tests accept
+ * any bf16 value (and code) between those of act(z) -/+ a stated bound.
+ * ---------------------------------------------------------------------- */
+int oracle_activation(const uint16_t *z, int64_t n, int32_t kind, double *out) {
+  if (n < 0 || (kind != 1 && kind != 2)) return ORACLE_ERR_ARG;
+  for (int64_t i = 0; i < n; ++i) {
+    double v = (double)bf16_to_f32(z[i]);
+    /* GELU through erfc(-z / sqrt 2) = 1 + erf(z / sqrt 2): no cancellation
+       for negative z, where 1 + erf would lose every digit in fp64 too */
+    out[i] = kind == 1 ? v / (1.0 + exp(-v)) : 0.5 * v * erfc(-v / sqrt(2.0));
+  }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------
  * Single-scale calibration, the plain W8A8 baseline that DualScale is
  * measured against  [P2 deployment-cost table, INT8 baseline row; P1
  * limitations section: DualScale could be enabled per layer only where the

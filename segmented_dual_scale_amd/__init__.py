@@ -30,7 +30,8 @@ __all__ = [
     "segquant_gemm_kernel_for", "segquant_status_string", "segquant_last_error",
     "segquant_version", "SEGQ_Q_SIGNED", "SEGQ_Q_PLANES", "SEGQ_GEMM_AUTO",
     "SEGQ_GEMM_FORCE_TILE", "SEGQ_GEMM_FORCE_SMALLM", "SEGQ_GEMM_FUSED_QUANT",
-    "SEGQ_GEMM_SINGLE_SCALE", "segquant_calibrate_amax_single", "SEGQ_KERNEL_TILE", "SEGQ_KERNEL_SMALLM",
+    "SEGQ_GEMM_SINGLE_SCALE", "segquant_calibrate_amax_single",
+    "SEGQ_ACT_SILU", "SEGQ_ACT_GELU", "segquant_activate_quantize", "SEGQ_KERNEL_TILE", "SEGQ_KERNEL_SMALLM",
 ]
 
 SEGQ_OK = 0
@@ -49,6 +50,8 @@ SEGQ_GEMM_FORCE_TILE = 1
 SEGQ_GEMM_FORCE_SMALLM = 2
 SEGQ_GEMM_FUSED_QUANT = 4
 SEGQ_GEMM_SINGLE_SCALE = 8
+SEGQ_ACT_SILU = 1
+SEGQ_ACT_GELU = 2
 SEGQ_KERNEL_TILE = 1
 SEGQ_KERNEL_SMALLM = 2
 
@@ -80,6 +83,8 @@ def load_library():
     sig = {
         "segquant_calibrate_amax": [P, I64, I64, I64, I32, P, P, P, P],
         "segquant_calibrate_amax_single": [P, I64, I64, I64, I32, P, P, P, P],
+        "segquant_activate_quantize": [P, I64, I64, I64, I32, I32, P, P, P, P, I64, I32, P, I64,
+                                       P],
         "segquant_quantize_dualscale": [P, I64, I64, I64, I32, P, P, P, P, I64, I32, P],
         "segquant_quantize_weight": [P, I64, I64, I64, I32, P, P, I32, P, P, I32, P, P, P],
         "segquant_unpack_weight": [P, I64, I64, P, I64, P],
@@ -203,6 +208,36 @@ def segquant_quantize_dualscale(x, act_scales, kseg: Optional[Sequence[int]] = N
                                            layout, _stream(x)),
            "segquant_quantize_dualscale")
     return out
+
+
+def segquant_activate_quantize(z, act_kind: int, act_scales=None,
+                               kseg: Optional[Sequence[int]] = None,
+                               layout: int = SEGQ_Q_SIGNED, out=None, x_out=None,
+                               want_codes: bool = True):
+    """SiLU/GELU of bf16 pre-activation Z fused with the dual-scale
+    quantisation.  Returns (codes or None, x_out or None): codes as
+    segquant_quantize_dualscale (when act_scales is given and want_codes),
+    x_out the bf16 activation if a tensor is passed (or x_out=True to
+    allocate one)."""
+    import torch
+    lib = load_library()
+    M, K = z.shape
+    off, wid = _segs(kseg, K)
+    if want_codes and act_scales is not None and out is None:
+        ldq = (K + 15) // 16 * 16
+        shape = (M, ldq) if layout == SEGQ_Q_SIGNED else (2, M, ldq)
+        out = torch.empty(shape, dtype=torch.int8, device=z.device)
+    if not (want_codes and act_scales is not None):
+        out = None
+    if x_out is True:
+        x_out = torch.empty((M, K), dtype=torch.bfloat16, device=z.device)
+    ld_q = out.stride(-2) if out is not None else 0
+    ld_xo = _ld(x_out, "x_out") if x_out is not None else 0
+    _check(lib.segquant_activate_quantize(_ptr(z), M, K, _ld(z, "z"), act_kind, len(wid),
+                                          _arr_ptr(off), _arr_ptr(wid), _ptr(act_scales), _ptr(out),
+                                          ld_q, layout, _ptr(x_out), ld_xo, _stream(z)),
+           "segquant_activate_quantize")
+    return out, x_out
 
 
 def segquant_quantize_weight(w, kseg: Optional[Sequence[int]] = None,

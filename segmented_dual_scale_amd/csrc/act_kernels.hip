@@ -7,6 +7,11 @@
 //     plain W8A8 baseline that DualScale is compared with [P2 deployment-cost
 //     table, INT8 baseline row; P1 limitations section, enabling DualScale
 //     only where the polarity asymmetry calls for it], and
+//   * the producer-fused variant: SiLU or exact-erf GELU of a bf16
+//     pre-activation, rounded to bf16, then quantised, in one HBM pass, so
+//     the activated bf16 X never round-trips through memory (SiLU and GELU
+//     are where the polarity asymmetry comes from [P1 DualScale motivation;
+//     P2 section 3]), and
 //   * the standalone polarity split + dual-scale quantisation
 //     [P1 "DualScale" split and quantisation; P2 section 3, Q_dual], an
 //     HBM-streaming kernel: 2 bytes read and 1 (signed code) or 2 (two
@@ -41,6 +46,8 @@ struct ActArgs {
   int32_t n_kseg;
   int32_t single;        // quantise both signs with the + half's inverse
   SegTable ks;
+  uint16_t *x_out;       // producer-fused kernel: optional bf16 copy of the activation
+  int64_t ld_xo;
 };
 
 __device__ __forceinline__ v4u load_x8(const uint16_t *p) {
@@ -154,6 +161,77 @@ __global__ __launch_bounds__(256) void quantize_kernel(ActArgs a) {
   }
 }
 
+// Activation of one element in fp32 [P1/P2: the SiLU and GELU outputs whose
+// polarity asymmetry DualScale serves]: SiLU z / (1 + e^-z); GELU in its
+// exact form z/2 (1 + erf(z / sqrt 2)), evaluated as z/2 erfc(-z / sqrt 2)
+// (the same function; 1 + erf cancels to nothing in fp32 for z below about
+// -4, erfc keeps full relative precision).  Library expf / erfcf.
+template <int ACT>
+__device__ __forceinline__ float activate(float z) {
+  if (ACT == 1) return z / (1.0f + expf(-z));
+  return 0.5f * z * erfcf(z * -0.70710678118654752f);
+}
+
+// Two bf16 pre-activations (one dword) -> two bf16 activations (one dword).
+template <int ACT>
+__device__ __forceinline__ uint32_t activate2(uint32_t u) {
+  const uint32_t lo = f32_to_bf16_rne(activate<ACT>(bf16_lo(u)));
+  const uint32_t hi = f32_to_bf16_rne(activate<ACT>(bf16_hi(u)));
+  return lo | (hi << 16);
+}
+
+// ACT: 1 SiLU, 2 GELU.  WQ: write codes (PLANES: two planes, else signed);
+// WX: write the bf16 activation.
+template <int ACT, bool WQ, bool PLANES, bool WX>
+__global__ __launch_bounds__(256) void act_quantize_kernel(ActArgs a) {
+  const int seg = blockIdx.y;
+  const int64_t k0 = a.ks.off[seg], k1 = a.ks.end[seg];
+  const float inv_pos = WQ ? a.act[2 * a.n_kseg + seg] : 0.0f;
+  const float inv_neg = WQ ? (a.single ? inv_pos : a.act[3 * a.n_kseg + seg]) : 0.0f;
+  const int L = 1 << a.lanes_log2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane >> a.lanes_log2, col = lane & (L - 1);
+  const int rows_per_step = (64 >> a.lanes_log2) * (blockDim.x >> 6);
+  const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
+  const int64_t r1 = min(r0 + a.rows_per_block, a.M);
+  for (int64_t r = r0 + wave * (64 >> a.lanes_log2) + sub; r < r1; r += rows_per_step) {
+    const uint16_t *row = a.x + r * a.ld_x;
+    int8_t *qrow = WQ ? a.q + r * a.ld_q : nullptr;
+    uint16_t *xrow = WX ? a.x_out + r * a.ld_xo : nullptr;
+    int64_t k = k0 + 8 * col;
+    for (; k + 8 <= k1; k += 8 * L) {
+      const v4u z = load_x8(row + k);
+      v4u v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = activate2<ACT>(z[j]);
+      if (WX) *reinterpret_cast<v4u *>(xrow + k) = v;
+      if (WQ) {
+        if (PLANES) {
+          v2u p, n;
+          quant8_planes(v, inv_pos, inv_neg, p, n);
+          *reinterpret_cast<v2u *>(qrow + k) = p;
+          *reinterpret_cast<v2u *>(qrow + a.plane_stride + k) = n;
+        } else {
+          *reinterpret_cast<v2u *>(qrow + k) = quant8_signed(v, inv_pos, inv_neg);
+        }
+      }
+    }
+    for (int64_t kk = k; kk < k1 && kk < k + 8; ++kk) {
+      const uint32_t xb = f32_to_bf16_rne(activate<ACT>(__uint_as_float(load_bf16(row + kk) << 16)));
+      if (WX) xrow[kk] = (uint16_t)xb;
+      if (WQ) {
+        const int8_t code = (int8_t)(quant_magic(__uint_as_float(xb << 16), inv_pos, inv_neg) & 0xffu);
+        if (PLANES) {
+          qrow[kk] = code > 0 ? code : 0;
+          qrow[a.plane_stride + kk] = code < 0 ? code : 0;
+        } else {
+          qrow[kk] = code;
+        }
+      }
+    }
+  }
+}
+
 // Rows per workgroup and lanes per row for a segment layout: aim for about
 // 16K elements per workgroup on the widest segment.
 void plan_rows(int64_t M, const SegTable &ks, ActArgs &a) {
@@ -203,6 +281,36 @@ hipError_t launch_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x
     hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quantize(const uint16_t *z, int64_t M, int64_t K, int64_t ld_z, int32_t act,
+                               const SegTable &ks, const float *scales, int8_t *q, int64_t ld_q,
+                               int32_t layout, uint16_t *x_out, int64_t ld_xo, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  ActArgs a{};
+  a.x = z; a.M = M; a.K = K; a.ld_x = ld_z; a.act = scales; a.q = q; a.ld_q = ld_q;
+  a.n_kseg = ks.n; a.ks = ks;
+  a.plane_stride = layout ? M * ld_q : 0;
+  a.x_out = x_out; a.ld_xo = ld_xo;
+  plan_rows(M, ks, a);
+  dim3 grid((unsigned)((M + a.rows_per_block - 1) / a.rows_per_block), (unsigned)ks.n);
+  const bool wq = q != nullptr, wx = x_out != nullptr;
+#define SQ_ACTQ(ACT, WQ, PL, WX) \
+  hipLaunchKernelGGL((act_quantize_kernel<ACT, WQ, PL, WX>), grid, dim3(256), 0, s, a)
+#define SQ_ACTQ_ALL(ACT)                                  \
+  if (!wq) SQ_ACTQ(ACT, false, false, true);              \
+  else if (layout && wx) SQ_ACTQ(ACT, true, true, true);  \
+  else if (layout) SQ_ACTQ(ACT, true, true, false);       \
+  else if (wx) SQ_ACTQ(ACT, true, false, true);           \
+  else SQ_ACTQ(ACT, true, false, false);
+  if (act == 1) {
+    SQ_ACTQ_ALL(1)
+  } else {
+    SQ_ACTQ_ALL(2)
+  }
+#undef SQ_ACTQ_ALL
+#undef SQ_ACTQ
   return hipGetLastError();
 }
 

@@ -176,6 +176,37 @@ int segquant_quantize_dualscale(const uint16_t *x_bf16, int64_t M, int64_t K, in
                     "quantize launch");
 }
 
+int segquant_activate_quantize(const uint16_t *z_bf16, int64_t M, int64_t K, int64_t ld_z,
+                               int32_t act_kind, int32_t n_kseg, const int32_t *kseg_offset,
+                               const int32_t *kseg_width, const float *act_scales,
+                               int8_t *q_out, int64_t ld_q, int32_t q_layout, uint16_t *x_out,
+                               int64_t ld_xo, void *stream) {
+  int st = check_x(z_bf16, M, K, ld_z);
+  if (st) return st;
+  if (act_kind != SEGQ_ACT_SILU && act_kind != SEGQ_ACT_GELU)
+    return fail(SEGQ_ERR_SHAPE, "unknown act_kind %d", act_kind);
+  if (!q_out && !x_out) return fail(SEGQ_ERR_NULL, "neither q_out nor x_out is given");
+  if (q_out) {
+    if (!act_scales) return fail(SEGQ_ERR_NULL, "act_scales is NULL");
+    if (q_layout != SEGQ_Q_SIGNED && q_layout != SEGQ_Q_PLANES)
+      return fail(SEGQ_ERR_SHAPE, "unknown q_layout %d", q_layout);
+    if (ld_q < K) return fail(SEGQ_ERR_SHAPE, "ld_q %lld < K %lld", (long long)ld_q, (long long)K);
+    if (ld_q % 16 != 0)
+      return fail(SEGQ_ERR_ALIGN, "ld_q %lld is not a multiple of 16", (long long)ld_q);
+    if (!aligned16(q_out)) return fail(SEGQ_ERR_ALIGN, "q_out is not 16-byte aligned");
+  }
+  if (x_out) {
+    if (ld_xo < K) return fail(SEGQ_ERR_SHAPE, "ld_xo %lld < K %lld", (long long)ld_xo, (long long)K);
+    if (ld_xo % 8 != 0 || !aligned16(x_out))
+      return fail(SEGQ_ERR_ALIGN, "x_out must be 16-byte aligned with ld_xo a multiple of 8");
+  }
+  sq::SegTable ks{};
+  if ((st = read_kseg(n_kseg, kseg_offset, kseg_width, K, 0, ks))) return st;
+  return hip_status(sq::launch_act_quantize(z_bf16, M, K, ld_z, act_kind, ks, act_scales, q_out,
+                                            ld_q, q_layout, x_out, ld_xo, (hipStream_t)stream),
+                    "activate-quantize launch");
+}
+
 int segquant_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w,
                              int32_t n_kseg, const int32_t *kseg_offset,
                              const int32_t *kseg_width, int32_t n_nseg,

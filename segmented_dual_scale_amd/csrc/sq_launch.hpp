@@ -32,6 +32,12 @@ hipError_t launch_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x
                            const SegTable &ks, const float *act, int8_t *q, int64_t ld_q,
                            int32_t layout, bool single, hipStream_t s);
 
+// act: 1 SiLU, 2 GELU.  q (codes, with scales) and x_out (bf16 activation)
+// are each optional; at least one is given.
+hipError_t launch_act_quantize(const uint16_t *z, int64_t M, int64_t K, int64_t ld_z, int32_t act,
+                               const SegTable &ks, const float *scales, int8_t *q, int64_t ld_q,
+                               int32_t layout, uint16_t *x_out, int64_t ld_xo, hipStream_t s);
+
 hipError_t launch_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w,
                                   const SegTable &ks, const NSegTable &ns, bool per_column,
                                   int8_t *w_packed, float *w_scale, hipStream_t s);

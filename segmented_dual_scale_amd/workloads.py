@@ -130,6 +130,36 @@ def make_x(wl: Workload, seed: int = 0) -> np.ndarray:
     return f32_to_bf16_bits(x)
 
 
+def preact_kind(wl: Workload) -> Optional[str]:
+    """Activation that produces the workload's X from its pre-activation:
+    "silu" (c1, c2), "gelu" (c3, c5), or None (c4 has no activation)."""
+    return {1: "silu", 2: "silu", 3: "gelu", 5: "gelu"}.get(wl.index)
+
+
+def make_preact(wl: Workload, seed: int = 0) -> np.ndarray:
+    """The pre-activation z of an activation workload as bf16 bits [M][K]:
+    the same draws make_x passes through SiLU/GELU, rounded to bf16 (the
+    input of the producer-fused quantisation; X there is bf16(act(bf16 z)))."""
+    M, K = wl.M, wl.K
+    g0, g1 = rng_for(seed, wl.index, 0), rng_for(seed, wl.index, 1)
+    if wl.index == 1:
+        z = _normal(g1, (M, K))
+    elif wl.index == 2:
+        n_neg = int(math.floor(0.95 * K))
+        mu = np.full(K, 1.0, np.float32)
+        mu[g0.permutation(K)[:n_neg]] = -1.5
+        z = _normal(g1, (M, K)) + mu[None, :]
+    elif wl.index in (3, 5):
+        sigma = g0.lognormal(0.0, 0.5, K).astype(np.float32)
+        if wl.index == 3:
+            sigma[g0.permutation(K)[: int(math.floor(0.01 * K))]] *= 8.0
+        z = _normal(g1, (M, K))
+        z *= sigma[None, :]
+    else:
+        raise ValueError(f"{wl.name} has no activation")
+    return f32_to_bf16_bits(z)
+
+
 def make_w(wl: Workload, seed: int = 0) -> np.ndarray:
     """Weight W of a named workload, fp32 [K][N]."""
     K, N = wl.K, wl.N

@@ -358,3 +358,54 @@ def test_discovered_segments_drive_the_layer():
         assert np.array_equal(acc.cpu().numpy(), ref.acc)
         ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), ref.y)
         assert ok, f"{type(mod).__name__}: {nbad} outputs out of tolerance, worst {worst}"
+
+
+# ------------------------------------- producer fused with quantisation ----
+ACTQ_CASES = [
+    # M, K, kseg, activation, z scale
+    (37, 512, [512], "gelu", 3.0),
+    (64, 1000, [512, 488], "silu", 2.0),      # ragged K: element-wise tail
+    (300, 1536, [64] * 24, "gelu", 1.5),
+    (5, 8200, [4096, 4104], "silu", 4.0),
+]
+
+
+@pytest.mark.parametrize("case", ACTQ_CASES, ids=[f"M{c[0]}_K{c[1]}_{c[3]}" for c in ACTQ_CASES])
+@pytest.mark.parametrize("layout", [S.SEGQ_Q_SIGNED, S.SEGQ_Q_PLANES])
+def test_activate_quantize_parity(case, layout):
+    """SiLU/GELU fused with the quantisation.  The bf16 activation the
+    kernel produces lies, element by element, between the bf16 roundings of
+    the fp64 activation minus and plus a bound on fp32 evaluation error
+    (2^-19 |act(z)|, a few fp32 ulps; bf16 spacing is 2^-8), and differs
+    from the rounding of the fp64 value in under 0.1 % of elements; its codes equal the
+    oracle's quantisation of those same bf16 values bit for bit; the
+    calibration on them is bit-exact; codes alone equal codes with the copy."""
+    import torch
+    M, K, kseg, kind, scale = case
+    z, _ = W.make_custom(M, K, 16, seed=K + M, kind="normal", x_scale=scale)
+    act_kind = S.SEGQ_ACT_SILU if kind == "silu" else S.SEGQ_ACT_GELU
+    zd = to_dev_bf16(z)
+    _, xdev = S.segquant_activate_quantize(zd, act_kind, kseg=kseg, x_out=True, want_codes=False)
+    torch.cuda.synchronize()
+    xb = xdev.view(torch.int16).cpu().numpy().view(np.uint16)
+    v = oracle.activation(z, kind)
+    delta = 2.0 ** -19 * np.abs(v) + 2.0 ** -140
+    lo = W.bf16_bits_to_f32(W.f32_to_bf16_bits((v - delta).astype(np.float32)))
+    hi = W.bf16_bits_to_f32(W.f32_to_bf16_bits((v + delta).astype(np.float32)))
+    xf = W.bf16_bits_to_f32(xb)
+    assert np.all((xf >= lo) & (xf <= hi)), "activation outside its error bound"
+    exact = W.bf16_bits_to_f32(W.f32_to_bf16_bits(v.astype(np.float32)))
+    assert np.mean(xf != exact) < 1e-3
+    # calibration on the produced values, then the fused codes
+    act = S.segquant_calibrate_amax(xdev, kseg)
+    sp, sn, ip, ineg = oracle.calibrate_amax(xb, kseg)
+    assert np.array_equal(act.cpu().numpy().view(np.uint32),
+                          np.stack([sp, sn, ip, ineg]).view(np.uint32))
+    qp, qn = oracle.quantize_dualscale(xb, kseg, ip, ineg)
+    q1, x2 = S.segquant_activate_quantize(zd, act_kind, act, kseg, layout, x_out=True)
+    q2, _ = S.segquant_activate_quantize(zd, act_kind, act, kseg, layout)
+    torch.cuda.synchronize()
+    assert torch.equal(x2, xdev)
+    for q in (q1, q2):
+        gp, gn = _q_planes_from_dev(q, layout, M, K)
+        assert np.array_equal(gp, qp) and np.array_equal(gn, qn), "fused codes differ"

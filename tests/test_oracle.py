@@ -409,6 +409,41 @@ def test_single_scale_layer_is_textbook_w8a8(kseg):
     np.testing.assert_allclose(y, yt, rtol=1e-12, atol=0)
 
 
+# ------------------------------------------------ producer activations ----
+@pytest.mark.parametrize("kind", ["silu", "gelu"])
+def test_activation_matches_library_and_odd_part(kind):
+    """[P1/P2: the SiLU/GELU producers of the asymmetric activations]
+    act(0) = 0; act(z) - act(-z) = z for both (sigma(z) + sigma(-z) = 1,
+    erf odd); and the values agree with torch's own fp64 functions."""
+    import torch
+    g = np.random.default_rng(5)
+    zf = np.concatenate([g.standard_normal(4000).astype(np.float32) * 3,
+                         np.array([0.0, 1.0, -1.0, 8.0, -8.0, 30.0, -30.0], np.float32)])
+    z = bits(zf)
+    v = oracle.activation(z, kind)
+    vn = oracle.activation(bits(-fl(z)), kind)
+    zz = fl(z).astype(np.float64)
+    np.testing.assert_allclose(v - vn, zz, rtol=1e-14, atol=1e-300)
+    assert oracle.activation(bits(np.zeros(1, np.float32)), kind)[0] == 0.0
+    # torch's fp64 functions where their own evaluation is accurate (its
+    # GELU goes through 1 + erf, which cancels for z below about -5)
+    t = torch.from_numpy(zz)
+    ref = (torch.nn.functional.silu(t) if kind == "silu" else torch.nn.functional.gelu(t)).numpy()
+    ok = zz > -5.0
+    np.testing.assert_allclose(v[ok], ref[ok], rtol=1e-9, atol=1e-300)
+    pos = zz >= 0
+    np.testing.assert_allclose(v[pos], ref[pos], rtol=1e-14, atol=1e-300)
+    if kind == "gelu":
+        # far left tail: GELU(z) = -phi(z) (1 - z^-2 + 3 z^-4 - 15 z^-6 + ...),
+        # phi the standard normal density (asymptotic series of erfc)
+        zt = np.array([-12.0, -20.0, -30.0], np.float32)
+        vt = oracle.activation(bits(zt), kind)
+        zz = zt.astype(np.float64)
+        phi = np.exp(-zz * zz / 2) / math.sqrt(2 * math.pi)
+        series = -phi * (1 - zz ** -2 + 3 * zz ** -4 - 15 * zz ** -6 + 105 * zz ** -8)
+        np.testing.assert_allclose(vt, series, rtol=1e-6)
+
+
 def test_composed_linear_equals_steps():
     x, w = W.make_custom(23, 256, 48, seed=19, kind="blocks")
     kseg = [64, 64, 128]
