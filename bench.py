@@ -158,7 +158,8 @@ class Layer:
         self.S, self.mode = S, mode
         # single: the single-scale W8A8 baseline (one symmetric scale per
         # segment, one product), bf16 input
-        self.flags = S.SEGQ_GEMM_SINGLE_SCALE if mode == "single" else S.SEGQ_GEMM_AUTO
+        self.flags = {"single": S.SEGQ_GEMM_SINGLE_SCALE, "w4": S.SEGQ_GEMM_W4}.get(
+            mode, S.SEGQ_GEMM_AUTO)
         wl, x, w = W.make_inputs(name)
         self.wl, self.x, self.w = wl, x, w
         self.kseg = list(wl.kseg)
@@ -168,13 +169,15 @@ class Layer:
         self.act = (S.segquant_calibrate_amax_single(xd, self.kseg) if mode == "single"
                     else S.segquant_calibrate_amax(xd, self.kseg))
         wd = torch.from_numpy(w).to(dev)
-        wp, self.ws = S.segquant_quantize_weight(wd, self.kseg, nseg, wl.per_column)
+        wp, self.ws = S.segquant_quantize_weight(wd, self.kseg, nseg, wl.per_column,
+                                                 bits=4 if mode == "w4" else 8)
         del wd
         self.layout = {"signed": S.SEGQ_Q_SIGNED, "planes": S.SEGQ_Q_PLANES}.get(mode)
+        self.w_bytes = wl.K * wl.N // (2 if mode == "w4" else 1)
         xq = S.segquant_quantize_dualscale(xd, self.act, self.kseg, self.layout) \
             if self.layout is not None else None
         torch.cuda.synchronize()
-        R = max(1, min(64, math.ceil(640e6 / alg_bytes(wl)))) if rotate else 1
+        R = max(1, min(64, math.ceil(640e6 / self.alg_bytes()))) if rotate else 1
         self.R = R
         if xq is None:
             self.xs = [xd] + [xd.clone() for _ in range(R - 1)]
@@ -255,10 +258,15 @@ class Layer:
         del graph
         return start.elapsed_time(end) / n, n
 
+    def alg_bytes(self) -> int:
+        """bf16 X + weight (int8, or 4-bit) + bf16 Y."""
+        wl = self.wl
+        return 2 * wl.M * wl.K + self.w_bytes + 2 * wl.M * wl.N
+
     def metrics(self, ms_per_step: float):
         wl = self.wl
         if hbm_bound(wl):
-            v = alg_bytes(wl) / (ms_per_step * 1e-3) / 1e9
+            v = self.alg_bytes() / (ms_per_step * 1e-3) / 1e9
             return {"value": v, "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
                     "frac": v / PEAK_HBM_GBS}
         v = alg_ops(wl) / (ms_per_step * 1e-3) / 1e12
@@ -502,10 +510,10 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--mode", default="bf16", choices=["bf16", "signed", "planes", "single"],
+    ap.add_argument("--mode", default="bf16", choices=["bf16", "signed", "planes", "single", "w4"],
                     help="bf16: the layer from bf16 input; signed/planes: time the GEMM on "
                          "an activation pre-quantised by segquant_quantize_dualscale; single: the "
-                         "single-scale W8A8 baseline from bf16 input")
+                         "single-scale W8A8 baseline from bf16 input; w4: W4A8 (4-bit weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch each step from Python")
     ap.add_argument("--no-all", action="store_true", help="skip the all_workloads summary")
@@ -574,7 +582,7 @@ def main():
     mk = layer.metrics(ms_kernel)
     roof = {"bound": mk["bound"], "achieved": mk["value"], "peak": mk["peak"], "unit": mk["unit"],
             "frac": mk["frac"], "traffic": None, "kernel": layer.kernel,
-            "per_launch": {"alg_bytes": alg_bytes(wl), "alg_int8_ops": alg_ops(wl),
+            "per_launch": {"alg_bytes": layer.alg_bytes(), "alg_int8_ops": alg_ops(wl),
                            "avg_us": ms_kernel * 1e3}}
     tr = read_traffic(layer.kernel, wl.name, args.mode)
     if tr is not None:
@@ -623,6 +631,16 @@ def main():
                 ms1, _ = lay.time(stream, 1, 10, use_graph, min_seconds=0.05)
                 summary[name]["single_scale_us_per_step"] = ms1 * 1e3
                 summary[name]["dualscale_over_single"] = ms / ms1
+                lay.free()
+                del lay
+                torch.cuda.empty_cache()
+                # W4A8: the same layer with 4-bit weights
+                lay = Layer(S, W, dev, name, "w4")
+                ms4, _ = lay.time(stream, 1, 10, use_graph, min_seconds=0.05)
+                m4 = lay.metrics(ms4)
+                summary[name]["w4a8"] = {"us_per_step": ms4 * 1e3, "value": m4["value"],
+                                         "unit": m4["unit"], "frac": m4["frac"],
+                                         "alg_bytes": lay.alg_bytes()}
                 lay.free()
                 del lay
                 torch.cuda.empty_cache()

@@ -88,6 +88,7 @@ extern "C" {
 #define SEGQ_GEMM_FUSED_QUANT 4u  /* quantise bf16 input inside the GEMM kernel
                                      even when a workspace is given */
 #define SEGQ_GEMM_SINGLE_SCALE 8u /* single-scale W8A8: see segquant_gemm_w8a8_seg */
+#define SEGQ_GEMM_W4 16u          /* w_packed holds 4-bit weights (segquant_quantize_weight_w4) */
 
 /* Kernel choices reported by segquant_gemm_kernel_for. */
 #define SEGQ_KERNEL_TILE 1
@@ -207,6 +208,33 @@ int segquant_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w,
                              void *stream);
 
 /*
+ * segquant_quantize_weight_w4 -- the 4-bit weights of W4A8, the pages'
+ * second precision [P2 deployment-cost table, SegQuant-4 row; P1
+ * experiments, W4A8], with the same groups as segquant_quantize_weight:
+ *   s_w = a/7, inv_w = 7/a, w_q = clamp(rne(fp32(w * inv_w)), -7, 7)
+ * Packed in 512-byte tiles that mirror the int8 ones (tile (nt, kt) at byte
+ * (nt * K/64 + kt) * 512; lane l = g*16 + j of a tile owns bytes l*8 .. l*8+7
+ * holding W_q[kt*64 + g*16 + b][nt*16 + j], b = 0..15, as codes + 8 in
+ * nibbles: byte i (i = 0..3) of the first dword holds b = i in its low and
+ * b = i + 4 in its high nibble, byte i of the second dword b = 8 + i and
+ * b = 12 + i).  segquant_weight_packed_bytes_w4(K, N) = K*N/2 bytes.
+ * Arguments, w_scale and launches as segquant_quantize_weight.
+ */
+int segquant_quantize_weight_w4(const float *w, int64_t K, int64_t N, int64_t ld_w,
+                                int32_t n_kseg, const int32_t *kseg_offset,
+                                const int32_t *kseg_width, int32_t n_nseg,
+                                const int32_t *nseg_offset, const int32_t *nseg_width,
+                                int32_t per_column, int8_t *w_packed, float *w_scale,
+                                void *stream);
+
+size_t segquant_weight_packed_bytes_w4(int64_t K, int64_t N);
+
+/* segquant_unpack_weight_w4 -- 4-bit packed weights -> int8 codes
+ * [K][ld_w] row-major (values in [-7, 7]).  For inspection and tests. */
+int segquant_unpack_weight_w4(const int8_t *w_packed, int64_t K, int64_t N, int8_t *w_kn,
+                              int64_t ld_w, void *stream);
+
+/*
  * segquant_unpack_weight -- inverse of the packing: w_packed -> device int8
  * W_q [K][ld_w] row-major.  For inspection and tests.  One launch.
  */
@@ -253,6 +281,13 @@ int segquant_unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t 
  *              of that table.  acc_debug then receives A_i in plane 0 and
  *              plane 1 is not written.  Takes bf16 or SEGQ_Q_SIGNED input
  *              (SEGQ_Q_PLANES: SEGQ_ERR_UNSUPPORTED).
+ *              SEGQ_GEMM_W4: w_packed is from segquant_quantize_weight_w4
+ *              (W4A8; same formula with the 4-bit codes).  The small-M
+ *              streaming kernel reads the 4-bit tiles directly (half the
+ *              weight bytes); every other shape first widens them to int8
+ *              tiles in the workspace, which must then hold K*N bytes (plus
+ *              the quantise-first bytes; segquant_gemm_workspace_bytes with
+ *              the same flags gives the total), else SEGQ_ERR_UNSUPPORTED.
  * Requires K % 64 == 0, N % 16 == 0, every K-segment width <=
  * SEGQ_MAX_KSEG_WIDTH (and, with more than one K-segment, K itself <=
  * SEGQ_MAX_KSEG_WIDTH: SEGQ_ERR_UNSUPPORTED otherwise, as the large-M kernel

@@ -58,11 +58,12 @@ def _load():
     lib.oracle_activation.argtypes = [P, I64, I32, P]
     lib.oracle_quantize_dualscale.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, P]
     lib.oracle_quantize_weight.argtypes = [P, I64, I64, I64, I32, P, P, I32, P, P, I32, P, P]
+    lib.oracle_quantize_weight_w4.argtypes = [P, I64, I64, I64, I32, P, P, I32, P, P, I32, P, P]
     lib.oracle_segment_acc.argtypes = [P, P, P, I64, I64, I64, I32, P, P, P]
     lib.oracle_dequantize.argtypes = [P, I64, I64, I32, P, P, P, P]
     lib.oracle_dualscale_linear.argtypes = [P, I64, I64, I64, P, P, I64, I32, P, P, P, P, P, P, P]
     for f in ("oracle_calibrate_amax", "oracle_calibrate_amax_single", "oracle_activation",
-              "oracle_quantize_dualscale", "oracle_quantize_weight",
+              "oracle_quantize_dualscale", "oracle_quantize_weight", "oracle_quantize_weight_w4",
               "oracle_segment_acc", "oracle_dequantize", "oracle_dualscale_linear"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
@@ -145,8 +146,9 @@ def quantize_dualscale(x_bf16: np.ndarray, kseg: Sequence[int], inv_pos, inv_neg
 
 
 def quantize_weight(w: np.ndarray, kseg: Sequence[int], nseg: Sequence[int] | None,
-                    per_column: bool):
-    """Returns (w_q int8 [K][N], w_scale fp32 [n_kseg][N])."""
+                    per_column: bool, bits: int = 8):
+    """Returns (w_q int8 [K][N], w_scale fp32 [n_kseg][N]); bits=4: the
+    4-bit weights (codes in [-7, 7], s_w = amax/7)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     K, N = w.shape
     koff, kwid = _segs(kseg)
@@ -155,9 +157,9 @@ def quantize_weight(w: np.ndarray, kseg: Sequence[int], nseg: Sequence[int] | No
     noff, nwid = _segs(nseg)
     wq = np.empty((K, N), np.int8)
     ws = np.empty((len(kwid), N), np.float32)
-    _check(_load().oracle_quantize_weight(_ptr(w), K, N, N, len(kwid), _ptr(koff), _ptr(kwid),
-                                          len(nwid), _ptr(noff), _ptr(nwid), int(per_column),
-                                          _ptr(wq), _ptr(ws)), "quantize_weight")
+    fn = {8: _load().oracle_quantize_weight, 4: _load().oracle_quantize_weight_w4}[bits]
+    _check(fn(_ptr(w), K, N, N, len(kwid), _ptr(koff), _ptr(kwid), len(nwid), _ptr(noff),
+              _ptr(nwid), int(per_column), _ptr(wq), _ptr(ws)), "quantize_weight")
     return wq, ws
 
 

@@ -230,10 +230,14 @@ int oracle_quantize_dualscale(const uint16_t *x, int64_t M, int64_t K, int64_t l
  * Outputs: w_q int8 [K][N] and w_scale fp32 [n_kseg][N] (the s_w of the
  * group holding (segment i, column n)).
  * ---------------------------------------------------------------------- */
-int oracle_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ldw,
-                           int32_t n_kseg, const int32_t *koff, const int32_t *kwid,
-                           int32_t n_nseg, const int32_t *noff, const int32_t *nwid,
-                           int32_t per_column, int8_t *w_q, float *w_scale) {
+/* levels: 127 (int8) or 7 (the 4-bit weights of W4A8 [P2 deployment-cost
+ * table, SegQuant-4; P1 experiments, W4A8]; reading: the same groups,
+ * symmetric codes in [-7, 7]). */
+static int quantize_weight_levels(const float *w, int64_t K, int64_t N, int64_t ldw,
+                                  int32_t n_kseg, const int32_t *koff, const int32_t *kwid,
+                                  int32_t n_nseg, const int32_t *noff, const int32_t *nwid,
+                                  int32_t per_column, int8_t *w_q, float *w_scale,
+                                  int32_t levels) {
   if (K < 1 || N < 1 || ldw < N || !segs_ok(n_kseg, koff, kwid, K)) return ORACLE_ERR_ARG;
   if (!per_column && !segs_ok(n_nseg, noff, nwid, N)) return ORACLE_ERR_ARG;
   int32_t ng = per_column ? (int32_t)N : n_nseg;
@@ -248,14 +252,30 @@ int oracle_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ldw,
           if (v > a) a = v;
         }
       float s_w, inv_w;
-      range_scale((double)a, 127.0, &s_w, &inv_w);
+      range_scale((double)a, (double)levels, &s_w, &inv_w);
       for (int64_t n = n0; n < n1; ++n) w_scale[(int64_t)i * N + n] = s_w;
       for (int64_t k = koff[i]; k < (int64_t)koff[i] + kwid[i]; ++k)
         for (int64_t n = n0; n < n1; ++n)
-          w_q[k * N + n] = (int8_t)quant_code(w[k * ldw + n], inv_w, -127, 127);
+          w_q[k * N + n] = (int8_t)quant_code(w[k * ldw + n], inv_w, -levels, levels);
     }
   }
   return ORACLE_OK;
+}
+
+int oracle_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ldw,
+                           int32_t n_kseg, const int32_t *koff, const int32_t *kwid,
+                           int32_t n_nseg, const int32_t *noff, const int32_t *nwid,
+                           int32_t per_column, int8_t *w_q, float *w_scale) {
+  return quantize_weight_levels(w, K, N, ldw, n_kseg, koff, kwid, n_nseg, noff, nwid,
+                                per_column, w_q, w_scale, 127);
+}
+
+int oracle_quantize_weight_w4(const float *w, int64_t K, int64_t N, int64_t ldw,
+                              int32_t n_kseg, const int32_t *koff, const int32_t *kwid,
+                              int32_t n_nseg, const int32_t *noff, const int32_t *nwid,
+                              int32_t per_column, int8_t *w_q, float *w_scale) {
+  return quantize_weight_levels(w, K, N, ldw, n_kseg, koff, kwid, n_nseg, noff, nwid,
+                                per_column, w_q, w_scale, 7);
 }
 
 /* ------------------------------------------------------------------------

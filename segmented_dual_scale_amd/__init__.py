@@ -31,7 +31,7 @@ __all__ = [
     "segquant_version", "SEGQ_Q_SIGNED", "SEGQ_Q_PLANES", "SEGQ_GEMM_AUTO",
     "SEGQ_GEMM_FORCE_TILE", "SEGQ_GEMM_FORCE_SMALLM", "SEGQ_GEMM_FUSED_QUANT",
     "SEGQ_GEMM_SINGLE_SCALE", "segquant_calibrate_amax_single",
-    "SEGQ_ACT_SILU", "SEGQ_ACT_GELU", "segquant_activate_quantize", "SEGQ_KERNEL_TILE", "SEGQ_KERNEL_SMALLM",
+    "SEGQ_ACT_SILU", "SEGQ_ACT_GELU", "segquant_activate_quantize", "SEGQ_GEMM_W4", "SEGQ_KERNEL_TILE", "SEGQ_KERNEL_SMALLM",
 ]
 
 SEGQ_OK = 0
@@ -50,6 +50,7 @@ SEGQ_GEMM_FORCE_TILE = 1
 SEGQ_GEMM_FORCE_SMALLM = 2
 SEGQ_GEMM_FUSED_QUANT = 4
 SEGQ_GEMM_SINGLE_SCALE = 8
+SEGQ_GEMM_W4 = 16
 SEGQ_ACT_SILU = 1
 SEGQ_ACT_GELU = 2
 SEGQ_KERNEL_TILE = 1
@@ -88,6 +89,9 @@ def load_library():
         "segquant_quantize_dualscale": [P, I64, I64, I64, I32, P, P, P, P, I64, I32, P],
         "segquant_quantize_weight": [P, I64, I64, I64, I32, P, P, I32, P, P, I32, P, P, P],
         "segquant_unpack_weight": [P, I64, I64, P, I64, P],
+        "segquant_unpack_weight_w4": [P, I64, I64, P, I64, P],
+        "segquant_quantize_weight_w4": [P, I64, I64, I64, I32, P, P, I32, P, P, I32, P, P, P],
+        "segquant_weight_packed_bytes_w4": [I64, I64],
         "segquant_gemm_w8a8_seg": [I64, I64, I64, P, I64, P, I64, I32, P, P, I32, P, P, P, P, I64,
                                    P, P, ctypes.c_size_t, U32, P],
         "segquant_gemm_workspace_bytes": [I64, I64, I64, I32, P, P, U32],
@@ -104,6 +108,7 @@ def load_library():
     lib.segquant_status_string.restype = ctypes.c_char_p
     lib.segquant_last_error.restype = ctypes.c_char_p
     lib.segquant_weight_packed_bytes.restype = ctypes.c_size_t
+    lib.segquant_weight_packed_bytes_w4.restype = ctypes.c_size_t
     lib.segquant_gemm_workspace_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
@@ -242,36 +247,40 @@ def segquant_activate_quantize(z, act_kind: int, act_scales=None,
 
 def segquant_quantize_weight(w, kseg: Optional[Sequence[int]] = None,
                              nseg: Optional[Sequence[int]] = None, per_column: bool = False,
-                             out_packed=None, out_scale=None) -> Tuple:
-    """Per-group symmetric int8 quantisation of fp32 W [K][N] (device):
-    returns (packed int8 weight, fp32 w_scale [n_kseg][N])."""
+                             out_packed=None, out_scale=None, bits: int = 8) -> Tuple:
+    """Per-group symmetric int8 (bits=8) or 4-bit (bits=4, W4A8) quantisation
+    of fp32 W [K][N] (device): returns (packed weight, fp32 w_scale
+    [n_kseg][N])."""
     import torch
     lib = load_library()
+    if bits not in (4, 8):
+        raise ValueError("bits must be 8 or 4")
     K, N = w.shape
     koff, kwid = _segs(kseg, K)
     noff, nwid = _segs(nseg, N)
     if out_packed is None:
-        nbytes = segquant_weight_packed_bytes(K, N)
+        nbytes = (segquant_weight_packed_bytes(K, N) if bits == 8
+                  else int(lib.segquant_weight_packed_bytes_w4(K, N)))
         out_packed = torch.empty(max(nbytes, 16), dtype=torch.int8, device=w.device)
     if out_scale is None:
         out_scale = torch.empty((len(kwid), N), dtype=torch.float32, device=w.device)
-    _check(lib.segquant_quantize_weight(_ptr(w), K, N, _ld(w, "w"), len(kwid), _arr_ptr(koff),
-                                        _arr_ptr(kwid), len(nwid), _arr_ptr(noff), _arr_ptr(nwid),
-                                        int(bool(per_column)), _ptr(out_packed), _ptr(out_scale),
-                                        _stream(w)),
-           "segquant_quantize_weight")
+    fn = lib.segquant_quantize_weight if bits == 8 else lib.segquant_quantize_weight_w4
+    _check(fn(_ptr(w), K, N, _ld(w, "w"), len(kwid), _arr_ptr(koff), _arr_ptr(kwid), len(nwid),
+              _arr_ptr(noff), _arr_ptr(nwid), int(bool(per_column)), _ptr(out_packed),
+              _ptr(out_scale), _stream(w)),
+           "segquant_quantize_weight" + ("" if bits == 8 else "_w4"))
     return out_packed, out_scale
 
 
-def segquant_unpack_weight(w_packed, K: int, N: int, out=None):
-    """Packed weight -> int8 W_q [K][N] (for inspection)."""
+def segquant_unpack_weight(w_packed, K: int, N: int, out=None, bits: int = 8):
+    """Packed weight (int8, or 4-bit with bits=4) -> int8 W_q [K][N]."""
     import torch
     lib = load_library()
     if out is None:
         out = torch.empty((K, N), dtype=torch.int8, device=w_packed.device)
-    _check(lib.segquant_unpack_weight(_ptr(w_packed), K, N, _ptr(out), _ld(out, "out"),
-                                      _stream(w_packed)),
-           "segquant_unpack_weight")
+    fn = lib.segquant_unpack_weight if bits == 8 else lib.segquant_unpack_weight_w4
+    _check(fn(_ptr(w_packed), K, N, _ptr(out), _ld(out, "out"), _stream(w_packed)),
+           "segquant_unpack_weight" + ("" if bits == 8 else "_w4"))
     return out
 
 
@@ -317,7 +326,7 @@ def segquant_gemm_w8a8_seg(x, w_packed, w_scale, act_scales, kseg: Optional[Sequ
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be a tensor, None or 'auto'")
-        nb = segquant_gemm_workspace_bytes(M, N, K, kseg, flags) if x is not None else 0
+        nb = segquant_gemm_workspace_bytes(M, N, K, kseg, flags)
         workspace = torch.empty(nb, dtype=torch.uint8, device=src.device) if nb else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.segquant_gemm_w8a8_seg(M, N, K, _ptr(x), ld_x, _ptr(xq), ld_q, q_layout,

@@ -126,6 +126,10 @@ const char *segquant_last_error(void) { return g_err.c_str(); }
 
 int segquant_version(void) { return 100; }
 
+size_t segquant_weight_packed_bytes_w4(int64_t K, int64_t N) {
+  return segquant_weight_packed_bytes(K, N) / 2;
+}
+
 size_t segquant_weight_packed_bytes(int64_t K, int64_t N) {
   if (K < 64 || N < 16 || K % 64 || N % 16 || K > kI32Max || N > kI32Max) return 0;
   return (size_t)K * (size_t)N;
@@ -207,12 +211,11 @@ int segquant_activate_quantize(const uint16_t *z_bf16, int64_t M, int64_t K, int
                     "activate-quantize launch");
 }
 
-int segquant_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w,
-                             int32_t n_kseg, const int32_t *kseg_offset,
-                             const int32_t *kseg_width, int32_t n_nseg,
-                             const int32_t *nseg_offset, const int32_t *nseg_width,
-                             int32_t per_column, int8_t *w_packed, float *w_scale,
-                             void *stream) {
+static int quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w, int32_t n_kseg,
+                           const int32_t *kseg_offset, const int32_t *kseg_width, int32_t n_nseg,
+                           const int32_t *nseg_offset, const int32_t *nseg_width,
+                           int32_t per_column, int8_t *w_packed, float *w_scale, bool w4,
+                           void *stream) {
   if (K < 1 || N < 1 || K > kI32Max || N > kI32Max)
     return fail(SEGQ_ERR_SHAPE, "bad shape K=%lld N=%lld", (long long)K, (long long)N);
   if (ld_w < N) return fail(SEGQ_ERR_SHAPE, "ld_w %lld < N %lld", (long long)ld_w, (long long)N);
@@ -231,20 +234,50 @@ int segquant_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w,
   ns.end[0] = (int32_t)N;
   if (!per_column && (st = read_nseg(n_nseg, nseg_offset, nseg_width, N, ns))) return st;
   return hip_status(sq::launch_quantize_weight(w, K, N, ld_w, ks, ns, per_column != 0, w_packed,
-                                               w_scale, (hipStream_t)stream),
+                                               w_scale, w4, (hipStream_t)stream),
                     "quantize_weight launch");
 }
 
-int segquant_unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t *w_kn,
-                           int64_t ld_w, void *stream) {
+int segquant_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w,
+                             int32_t n_kseg, const int32_t *kseg_offset,
+                             const int32_t *kseg_width, int32_t n_nseg,
+                             const int32_t *nseg_offset, const int32_t *nseg_width,
+                             int32_t per_column, int8_t *w_packed, float *w_scale,
+                             void *stream) {
+  return quantize_weight(w, K, N, ld_w, n_kseg, kseg_offset, kseg_width, n_nseg, nseg_offset,
+                         nseg_width, per_column, w_packed, w_scale, false, stream);
+}
+
+int segquant_quantize_weight_w4(const float *w, int64_t K, int64_t N, int64_t ld_w,
+                                int32_t n_kseg, const int32_t *kseg_offset,
+                                const int32_t *kseg_width, int32_t n_nseg,
+                                const int32_t *nseg_offset, const int32_t *nseg_width,
+                                int32_t per_column, int8_t *w_packed, float *w_scale,
+                                void *stream) {
+  return quantize_weight(w, K, N, ld_w, n_kseg, kseg_offset, kseg_width, n_nseg, nseg_offset,
+                         nseg_width, per_column, w_packed, w_scale, true, stream);
+}
+
+static int unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t *w_kn,
+                         int64_t ld_w, bool w4, void *stream) {
   if (segquant_weight_packed_bytes(K, N) == 0)
     return fail(SEGQ_ERR_ALIGN, "weight needs K %% 64 == 0 and N %% 16 == 0 (K=%lld N=%lld)",
                 (long long)K, (long long)N);
   if (ld_w < N) return fail(SEGQ_ERR_SHAPE, "ld_w %lld < N %lld", (long long)ld_w, (long long)N);
   if (!w_packed || !w_kn) return fail(SEGQ_ERR_NULL, "w_packed or w_kn is NULL");
   if (!aligned16(w_packed)) return fail(SEGQ_ERR_ALIGN, "w_packed is not 16-byte aligned");
-  return hip_status(sq::launch_unpack_weight(w_packed, K, N, w_kn, ld_w, (hipStream_t)stream),
+  return hip_status(sq::launch_unpack_weight(w_packed, K, N, w_kn, ld_w, w4, (hipStream_t)stream),
                     "unpack launch");
+}
+
+int segquant_unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t *w_kn,
+                           int64_t ld_w, void *stream) {
+  return unpack_weight(w_packed, K, N, w_kn, ld_w, false, stream);
+}
+
+int segquant_unpack_weight_w4(const int8_t *w_packed, int64_t K, int64_t N, int8_t *w_kn,
+                              int64_t ld_w, void *stream) {
+  return unpack_weight(w_packed, K, N, w_kn, ld_w, true, stream);
 }
 
 static int gemm_check(int64_t M, int64_t N, int64_t K, uint32_t flags) {
@@ -255,7 +288,7 @@ static int gemm_check(int64_t M, int64_t N, int64_t K, uint32_t flags) {
     return fail(SEGQ_ERR_ALIGN, "GEMM needs K %% 64 == 0 and N %% 16 == 0 (K=%lld N=%lld)",
                 (long long)K, (long long)N);
   if (flags & ~(SEGQ_GEMM_FORCE_TILE | SEGQ_GEMM_FORCE_SMALLM | SEGQ_GEMM_FUSED_QUANT |
-                SEGQ_GEMM_SINGLE_SCALE))
+                SEGQ_GEMM_SINGLE_SCALE | SEGQ_GEMM_W4))
     return fail(SEGQ_ERR_SHAPE, "unknown flags 0x%x", flags);
   if ((flags & SEGQ_GEMM_FORCE_TILE) && (flags & SEGQ_GEMM_FORCE_SMALLM))
     return fail(SEGQ_ERR_SHAPE, "both kernels forced");
@@ -279,6 +312,15 @@ static bool quantize_first(int kernel, int64_t M, int64_t N, const sq::SegTable 
          sq::tile_quantize_first(M, N, ks);
 }
 
+// Bytes of the widened int8 weight a W4 call needs in its workspace (0 when
+// the small-M streaming kernel reads the 4-bit tiles itself).
+static size_t w4_widen_bytes(int kernel, int64_t M, int64_t N, int64_t K, const sq::SegTable &ks,
+                             uint32_t flags, bool bf16_input) {
+  if (!(flags & SEGQ_GEMM_W4)) return 0;
+  if (kernel == SEGQ_KERNEL_SMALLM && sq::smallm_reads_w4(M, K, ks.n, bf16_input)) return 0;
+  return (size_t)K * (size_t)N;
+}
+
 size_t segquant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t n_kseg,
                                      const int32_t *kseg_offset, const int32_t *kseg_width,
                                      uint32_t flags) {
@@ -287,7 +329,8 @@ size_t segquant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t n_
   if (read_kseg(n_kseg, kseg_offset, kseg_width, K, SEGQ_MAX_KSEG_WIDTH, ks)) return 0;
   ok();
   const int kernel = segquant_gemm_kernel_for(M, N, K, flags);
-  return quantize_first(kernel, M, N, ks, flags) ? (size_t)(M * K) : 0;
+  return w4_widen_bytes(kernel, M, N, K, ks, flags, true) +
+         (quantize_first(kernel, M, N, ks, flags) ? (size_t)(M * K) : 0);
 }
 
 int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
@@ -342,10 +385,26 @@ int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
   p.y = y_bf16; p.ld_y = ld_y; p.acc_debug = acc_debug;
   p.single_scale = (flags & SEGQ_GEMM_SINGLE_SCALE) != 0;
   const int kernel = segquant_gemm_kernel_for(M, N, K, flags);
-  if (x_bf16 && workspace && quantize_first(kernel, M, N, ks, flags) &&
-      workspace_bytes >= (size_t)(M * K)) {
+  // 4-bit weights: the streaming small-M kernel reads them as they are;
+  // every other path first widens them to int8 tiles in the workspace
+  const size_t widen = w4_widen_bytes(kernel, M, N, K, ks, flags, x_bf16 != nullptr);
+  if (widen && (!workspace || workspace_bytes < widen))
+    return fail(SEGQ_ERR_UNSUPPORTED,
+                "4-bit weights on this shape need a workspace of at least %zu bytes "
+                "(segquant_gemm_workspace_bytes)", widen);
+  p.w4 = (flags & SEGQ_GEMM_W4) && !widen;
+  if (widen) {
+    int8_t *w8 = static_cast<int8_t *>(workspace);
+    hipError_t e = sq::launch_widen_w4(w_packed, K, N, w8, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "widen launch");
+    p.w_packed = w8;
+  }
+  uint8_t *ws_rest = workspace ? static_cast<uint8_t *>(workspace) + widen : nullptr;
+  const size_t ws_rest_bytes = workspace ? workspace_bytes - widen : 0;
+  if (x_bf16 && ws_rest && quantize_first(kernel, M, N, ks, flags) &&
+      ws_rest_bytes >= (size_t)(M * K)) {
     // quantise once into the workspace, then the GEMM from the signed codes
-    int8_t *codes = static_cast<int8_t *>(workspace);
+    int8_t *codes = reinterpret_cast<int8_t *>(ws_rest);
     hipError_t e = sq::launch_quantize(x_bf16, M, K, ld_x, ks, act_scales, codes, K,
                                        SEGQ_Q_SIGNED, p.single_scale, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "quantize launch");

@@ -281,7 +281,8 @@ struct StreamArgs {
 // four consecutive rows, each lane holds both halves of its two X rows: the
 // fold needs no data from other lanes.  Otherwise each half has its own A
 // operand (rows at or past M zero).
-template <int QL, int RING, bool SEG1, bool PACK, bool DEBUG>
+// W4: 4-bit weight tiles (512 bytes, 8 per lane), widened in registers.
+template <int QL, int RING, bool SEG1, bool PACK, bool W4, bool DEBUG>
 __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t planes[2 * kSmallMMax * kStreamPitch];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -329,11 +330,15 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   // (3) the whole weight stream of this wave (the scheduling barriers keep
   //     the loads above ahead of it in issue order)
   __builtin_amdgcn_sched_barrier(0);
-  const int8_t *wcol = a.w + (int64_t)ntc * KT * 1024 + lane * 16;
-  v4u ring[RING];
+  constexpr int kTileBytes = W4 ? 512 : 1024;
+  const int8_t *wcol = a.w + (int64_t)ntc * KT * kTileBytes + lane * (W4 ? 8 : 16);
+  v4u ring[W4 ? 1 : RING];
+  v2u ring4[W4 ? RING : 1];
 #pragma unroll
   for (int d = 0; d < RING; ++d) {
-    ring[d] = *reinterpret_cast<const v4u *>(wcol + (int64_t)min(d, KT - 1) * 1024);
+    const int8_t *src = wcol + (int64_t)min(d, KT - 1) * kTileBytes;
+    if (W4) ring4[W4 ? d : 0] = *reinterpret_cast<const v2u *>(src);
+    else ring[W4 ? 0 : d] = *reinterpret_cast<const v4u *>(src);
     __builtin_amdgcn_sched_barrier(0);  // in tile order, as the chain below waits for them
   }
 
@@ -473,7 +478,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
     for (int r = 0; r < 4; ++r)
       yacc[r] = __builtin_fmaf(cn, (float)Q[r], __builtin_fmaf(cp, (float)P[r], yacc[r]));
   };
-  auto wtile = [&](int t) { return ring[t]; };
+  auto wtile = [&](int t) { return W4 ? unpack_w4(ring4[W4 ? t : 0]) : ring[W4 ? 0 : t]; };
   auto mfma = [](const v4u &x, const v4u &w, const v4i &c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(reinterpret_cast<const v4i &>(x),
                                                  reinterpret_cast<const v4i &>(w), c, 0, 0, 0);
@@ -533,11 +538,11 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   }
 }
 
-template <int RING, bool SEG1, bool PACK>
+template <int RING, bool SEG1, bool PACK, bool W4>
 void launch_stream_ring(const StreamArgs &a, int ql, bool debug, dim3 grid, hipStream_t s) {
-#define SQ_STREAM(QLV, DBG)                                                                   \
-  hipLaunchKernelGGL((gemm_smallm_kernel<QLV, RING, SEG1, PACK, DBG>), grid, dim3(kStreamThreads), \
-                     0, s, a)
+#define SQ_STREAM(QLV, DBG)                                                           \
+  hipLaunchKernelGGL((gemm_smallm_kernel<QLV, RING, SEG1, PACK, W4, DBG>), grid,      \
+                     dim3(kStreamThreads), 0, s, a)
   if (debug) {
     if (ql < 0) SQ_STREAM(-1, true);
     else if (ql == 0) SQ_STREAM(0, true);
@@ -550,24 +555,27 @@ void launch_stream_ring(const StreamArgs &a, int ql, bool debug, dim3 grid, hipS
 #undef SQ_STREAM
 }
 
-template <int RING>
-void launch_stream_segs(const StreamArgs &a, int ql, bool debug, dim3 grid, hipStream_t s) {
+template <int RING, bool W4>
+void launch_stream_w(const StreamArgs &a, int ql, bool debug, dim3 grid, hipStream_t s) {
   const bool pack = a.M <= 8;
   if (a.n_kseg == 1) {
-    if (pack) launch_stream_ring<RING, true, true>(a, ql, debug, grid, s);
-    else launch_stream_ring<RING, true, false>(a, ql, debug, grid, s);
+    if (pack) launch_stream_ring<RING, true, true, W4>(a, ql, debug, grid, s);
+    else launch_stream_ring<RING, true, false, W4>(a, ql, debug, grid, s);
   } else {
-    if (pack) launch_stream_ring<RING, false, true>(a, ql, debug, grid, s);
-    else launch_stream_ring<RING, false, false>(a, ql, debug, grid, s);
+    if (pack) launch_stream_ring<RING, false, true, W4>(a, ql, debug, grid, s);
+    else launch_stream_ring<RING, false, false, W4>(a, ql, debug, grid, s);
   }
 }
 
-// Shapes the streaming kernel takes; the rest go to the chunked kernel.
-bool stream_fits(const GemmProblem &p) {
-  const int64_t KT = p.K / 64;
-  const int64_t ppr = p.x ? p.K / 8 : p.K / 16;
-  return KT <= kStreamMaxKT && p.ks.n <= kStreamMaxKT && p.M * ppr <= kStreamXR * kStreamThreads;
+template <int RING>
+void launch_stream_segs(const StreamArgs &a, int ql, bool debug, bool w4, dim3 grid,
+                        hipStream_t s) {
+  if (w4) launch_stream_w<RING, true>(a, ql, debug, grid, s);
+  else launch_stream_w<RING, false>(a, ql, debug, grid, s);
 }
+
+// Shapes the streaming kernel takes; the rest go to the chunked kernel.
+bool stream_fits(const GemmProblem &p) { return smallm_reads_w4(p.M, p.K, p.ks.n, p.x != nullptr); }
 
 hipError_t launch_stream(const GemmProblem &p, hipStream_t s) {
   StreamArgs a{};
@@ -599,14 +607,20 @@ hipError_t launch_stream(const GemmProblem &p, hipStream_t s) {
   const int KT = (int)(p.K / 64);
   const dim3 grid((unsigned)((p.N / 16 + 3) / 4));
   const bool debug = p.acc_debug != nullptr;
-  if (KT <= 8) launch_stream_segs<8>(a, ql, debug, grid, s);
-  else if (KT <= 16) launch_stream_segs<16>(a, ql, debug, grid, s);
-  else if (KT <= 24) launch_stream_segs<24>(a, ql, debug, grid, s);
-  else launch_stream_segs<32>(a, ql, debug, grid, s);
+  if (KT <= 8) launch_stream_segs<8>(a, ql, debug, p.w4, grid, s);
+  else if (KT <= 16) launch_stream_segs<16>(a, ql, debug, p.w4, grid, s);
+  else if (KT <= 24) launch_stream_segs<24>(a, ql, debug, p.w4, grid, s);
+  else launch_stream_segs<32>(a, ql, debug, p.w4, grid, s);
   return hipGetLastError();
 }
 
 }  // namespace
+
+bool smallm_reads_w4(int64_t M, int64_t K, int n_kseg, bool bf16_input) {
+  const int64_t KT = K / 64;
+  const int64_t ppr = bf16_input ? K / 8 : K / 16;
+  return KT <= kStreamMaxKT && n_kseg <= kStreamMaxKT && M * ppr <= kStreamXR * kStreamThreads;
+}
 
 hipError_t launch_gemm_smallm(const GemmProblem &p, hipStream_t s) {
   if (stream_fits(p)) return launch_stream(p, s);

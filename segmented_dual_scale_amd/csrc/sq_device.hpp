@@ -98,6 +98,21 @@ __device__ __forceinline__ void split_signed(uint32_t q, uint32_t &pos, uint32_t
   pos = q ^ neg;
 }
 
+// A 4-bit weight lane-row (8 bytes of codes biased by +8, so 1..15) -> the
+// 16 signed int8 bytes of its matrix-core operand.  In each dword the low
+// nibbles are operand bytes 0-3 and the high nibbles bytes 4-7 of that
+// half; (v + 0x78) ^ 0x80 maps a biased nibble v to the byte v - 8 with no
+// carry between bytes (v + 0x78 <= 0x87).
+__device__ __forceinline__ v4u unpack_w4(v2u u) {
+  v4u o;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    o[2 * h] = ((u[h] & 0x0f0f0f0fu) + 0x78787878u) ^ 0x80808080u;
+    o[2 * h + 1] = (((u[h] >> 4) & 0x0f0f0f0fu) + 0x78787878u) ^ 0x80808080u;
+  }
+  return o;
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite values; NaN stays NaN).
 // A select, not a branch: in a store epilogue the branch cost more than the
 // arithmetic.

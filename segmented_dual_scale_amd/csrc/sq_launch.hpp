@@ -38,12 +38,16 @@ hipError_t launch_act_quantize(const uint16_t *z, int64_t M, int64_t K, int64_t 
                                const SegTable &ks, const float *scales, int8_t *q, int64_t ld_q,
                                int32_t layout, uint16_t *x_out, int64_t ld_xo, hipStream_t s);
 
+// w4: 4-bit codes in the nibble layout (K*N/2 bytes) instead of int8
 hipError_t launch_quantize_weight(const float *w, int64_t K, int64_t N, int64_t ld_w,
                                   const SegTable &ks, const NSegTable &ns, bool per_column,
-                                  int8_t *w_packed, float *w_scale, hipStream_t s);
+                                  int8_t *w_packed, float *w_scale, bool w4, hipStream_t s);
 
 hipError_t launch_unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t *w_kn,
-                                int64_t ld_w, hipStream_t s);
+                                int64_t ld_w, bool w4, hipStream_t s);
+
+// 4-bit packed tiles -> int8 packed tiles (K*N bytes)
+hipError_t launch_widen_w4(const int8_t *w4, int64_t K, int64_t N, int8_t *w8, hipStream_t s);
 
 struct GemmProblem {
   int64_t M, N, K;
@@ -60,12 +64,17 @@ struct GemmProblem {
   int64_t ld_y;
   int32_t *acc_debug;
   bool single_scale;  // one product on the signed code, + half's scales only
+  bool w4;            // w_packed holds 4-bit codes (small-M streaming kernel only)
 };
 
 hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s);
 hipError_t launch_gemm_smallm(const GemmProblem &p, hipStream_t s);
 
 constexpr int kSmallMMax = 16;
+
+// Whether the streaming small-M kernel takes this shape (and so reads
+// 4-bit weight tiles directly).
+bool smallm_reads_w4(int64_t M, int64_t K, int n_kseg, bool bf16_input);
 
 // Output columns per workgroup of the tile kernel for these K-segments.
 int tile_columns(const SegTable &ks);

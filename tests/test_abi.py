@@ -128,12 +128,24 @@ def gemm(M=64, N=64, K=128, x=FAKE, ld_x=None, xq=None, ld_q=0, q_layout=0, w=FA
     (dict(K=132160, widths=[66048, 66112]), S.SEGQ_ERR_UNSUPPORTED),  # running sums over all of K
     (dict(M=17, flags=S.SEGQ_GEMM_FORCE_SMALLM), S.SEGQ_ERR_UNSUPPORTED),
     (dict(flags=3), S.SEGQ_ERR_SHAPE),
-    (dict(flags=16), S.SEGQ_ERR_SHAPE),
+    (dict(flags=32), S.SEGQ_ERR_SHAPE),
     (dict(x=None, xq=FAKE, ld_q=128, q_layout=1, flags=8), S.SEGQ_ERR_UNSUPPORTED),
 ])
 def test_gemm_validation(kwargs, status):
     assert gemm(**kwargs) == status
     assert S.segquant_last_error() != ""
+
+
+def test_gemm_w4_needs_a_workspace_off_the_streaming_kernel():
+    """4-bit weights on a large-M shape are widened in the workspace first:
+    without one (or with too small a one) the call fails before any launch."""
+    assert gemm(M=64, flags=S.SEGQ_GEMM_W4) == S.SEGQ_ERR_UNSUPPORTED
+    assert "workspace" in S.segquant_last_error()
+    assert gemm(M=64, flags=S.SEGQ_GEMM_W4, work=FAKE, work_bytes=64 * 128 - 16) == S.SEGQ_ERR_UNSUPPORTED
+    assert S.segquant_gemm_workspace_bytes(64, 64, 128, None, S.SEGQ_GEMM_W4) == 64 * 128
+    # the streaming small-M kernel reads the 4-bit tiles itself
+    assert S.segquant_gemm_workspace_bytes(2, 9216, 1536, None, S.SEGQ_GEMM_W4) == 0
+    assert S.segquant_weight_packed_bytes(1536, 9216) == 2 * S.load_library().segquant_weight_packed_bytes_w4(1536, 9216)
 
 
 def test_gemm_misaligned_workspace():

@@ -409,3 +409,54 @@ def test_activate_quantize_parity(case, layout):
     for q in (q1, q2):
         gp, gn = _q_planes_from_dev(q, layout, M, K)
         assert np.array_equal(gp, qp) and np.array_equal(gn, qn), "fused codes differ"
+
+
+# ------------------------------------------------------- 4-bit weights ----
+W4_CASES = [
+    # M, K, N, kseg, nseg, per_column, kind
+    (2, 1536, 576, [1536], [96] * 6, False, "silu"),     # streaming small-M kernel reads 4-bit tiles
+    (3, 256, 48, [64, 192], None, True, "blocks"),
+    (8, 2048, 64, [64] * 32, [64], False, "blocks"),
+    (16, 4096, 64, [4096], None, True, "gelu"),          # K past the streaming kernel: widened
+    (77, 384, 768, [128, 256], [256] * 3, False, "gelu"),  # tile kernel: widened in the workspace
+    (333, 512, 320, [512], None, True, "gelu"),
+]
+
+
+@pytest.mark.parametrize("case", W4_CASES, ids=[f"M{c[0]}_K{c[1]}_N{c[2]}_S{len(c[3])}" for c in W4_CASES])
+@pytest.mark.parametrize("mode", ["bf16", "signed"])
+def test_w4a8_parity(case, mode):
+    """W4A8: 4-bit weight codes and scales bit-exact against the oracle's
+    4-bit quantisation; per-segment accumulators bit-exact and Y within
+    tolerance, on the streaming kernel (4-bit tiles read directly) and on
+    the paths that widen them to int8 first."""
+    import torch
+    M, K, N, kseg, nseg, per_column, kind = case
+    x, w = W.make_custom(M, K, N, seed=M + 7 * K, kind=kind, x_scale=2.0)
+    sp, sn, ip, ineg = oracle.calibrate_amax(x, kseg)
+    wq, ws = oracle.quantize_weight(w, kseg, nseg, per_column, bits=4)
+    qp, qn = oracle.quantize_dualscale(x, kseg, ip, ineg)
+    acc_ref = oracle.segment_acc(qp, qn, wq, kseg)
+    y_ref = oracle.dequantize(acc_ref, sp, sn, ws)
+    xd = to_dev_bf16(x)
+    act = S.segquant_calibrate_amax(xd, kseg)
+    wp, gws = S.segquant_quantize_weight(to_dev(w), kseg, nseg, per_column, bits=4)
+    assert wp.numel() == K * N // 2
+    assert np.array_equal(S.segquant_unpack_weight(wp, K, N, bits=4).cpu().numpy(), wq)
+    assert np.array_equal(gws.cpu().numpy().view(np.uint32), ws.view(np.uint32))
+    xq = S.segquant_quantize_dualscale(xd, act, kseg, S.SEGQ_Q_SIGNED) if mode == "signed" else None
+    for debug in (True, False):
+        acc = (torch.full((2, len(kseg), M, N), -7, dtype=torch.int32, device=DEV)
+               if debug else None)
+        if mode == "bf16":
+            y = S.segquant_gemm_w8a8_seg(xd, wp, gws, act, kseg, N=N, acc_debug=acc,
+                                         flags=S.SEGQ_GEMM_W4)
+        else:
+            y = S.segquant_gemm_w8a8_seg(None, wp, gws, act, kseg, N=N, xq=xq,
+                                         q_layout=S.SEGQ_Q_SIGNED, acc_debug=acc,
+                                         flags=S.SEGQ_GEMM_W4)
+        torch.cuda.synchronize()
+        if debug:
+            assert np.array_equal(acc.cpu().numpy(), acc_ref), "W4A8 accumulators differ"
+        ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), y_ref)
+        assert ok, f"W4A8 Y out of tolerance (debug={debug}): {nbad} elements, worst {worst}"

@@ -444,6 +444,43 @@ def test_activation_matches_library_and_odd_part(kind):
         np.testing.assert_allclose(vt, series, rtol=1e-6)
 
 
+# ---------------------------------------------------- 4-bit weights (W4A8) ----
+def test_w4_weight_worked_example_and_ties():
+    """4-bit weights [P2 deployment-cost table, SegQuant-4; P1 W4A8]: one
+    group with amax 3.5 -> s_w = 0.5, inv_w = 2 (both exact).  Worked out by
+    hand: w = 3.5 -> 7; 1.25 -> 2.5 -> 2 (tie to even); 0.75 -> 1.5 -> 2;
+    -0.25 -> -0.5 -> -0 = 0 (tie to even); -1.75 -> -3.5 -> -4; -3.5 -> -7."""
+    w = np.array([[3.5], [1.25], [0.75], [-0.25], [-1.75], [-3.5]] + [[0.0]] * 58, np.float32)
+    wq, ws = oracle.quantize_weight(w, [64], None, True, bits=4)
+    assert ws[0, 0] == np.float32(0.5)
+    assert wq[:6, 0].tolist() == [7, 2, 2, 0, -4, -7]
+    assert not wq[6:].any()
+
+
+@pytest.mark.parametrize("per_column", [False, True])
+def test_w4_weight_groups_range_and_error(per_column):
+    """Codes in [-7, 7]; the largest |w| of each group maps to +-7; every
+    element within half a step of its reconstruction (up to the fp32
+    rounding of the product); groups as for int8 weights."""
+    g = np.random.default_rng(3)
+    K, N, kseg, nseg = 192, 48, [64, 128], [16, 32]
+    w = (g.standard_normal((K, N)) * np.repeat([0.02, 0.3], [16, 32])[None, :]).astype(np.float32)
+    wq, ws = oracle.quantize_weight(w, kseg, None if per_column else nseg, per_column, bits=4)
+    assert wq.min() >= -7 and wq.max() <= 7
+    w8, ws8 = oracle.quantize_weight(w, kseg, None if per_column else nseg, per_column, bits=8)
+    # same groups: the 4-bit step is the int8 step times 127/7 (each rounded once)
+    np.testing.assert_allclose(ws.astype(np.float64), ws8.astype(np.float64) * 127 / 7, rtol=2e-7)
+    rec = wq.astype(np.float64) * np.repeat(ws, kseg, axis=0)
+    step = np.repeat(ws, kseg, axis=0).astype(np.float64)
+    assert np.all(np.abs(rec - w) <= 0.5 * step * (1 + 1e-6) + 1e-12)
+    for i, (lo, hi) in enumerate([(0, 64), (64, 192)]):
+        groups = [(c, c + 1) for c in range(N)] if per_column else [(0, 16), (16, 48)]
+        for c0, c1 in groups:
+            blk = np.abs(w[lo:hi, c0:c1])
+            r, c = np.unravel_index(np.argmax(blk), blk.shape)
+            assert abs(int(wq[lo + r, c0 + c])) == 7
+
+
 def test_composed_linear_equals_steps():
     x, w = W.make_custom(23, 256, 48, seed=19, kind="blocks")
     kseg = [64, 64, 128]
