@@ -460,3 +460,37 @@ def test_w4a8_parity(case, mode):
             assert np.array_equal(acc.cpu().numpy(), acc_ref), "W4A8 accumulators differ"
         ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), y_ref)
         assert ok, f"W4A8 Y out of tolerance (debug={debug}): {nbad} elements, worst {worst}"
+
+
+# ------------------------------------------------------------ HIP graphs ----
+@pytest.mark.parametrize("name", ["c2_adanorm_gemv", "c4_attn_out_inseg"])
+def test_graph_replays_match_eager(name):
+    """The layer captured in a HIP graph (the benchmark's timed form; for c4
+    the two-launch quantise-first path with its workspace) and replayed
+    several times, with eager work and synchronisations between replays:
+    every replay's Y equals the eager call's bit for bit (same kernels, no
+    memset nodes)."""
+    import torch
+    wl, x, w = W.make_inputs(name)
+    nseg = None if wl.per_column else list(wl.nseg)
+    gpu = GpuLayer(x, w, wl.kseg, nseg, wl.per_column)
+    nb = S.segquant_gemm_workspace_bytes(wl.M, wl.N, wl.K, list(wl.kseg))
+    work = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV) if nb else None
+    out = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=DEV)
+    y_eager = S.segquant_gemm_w8a8_seg(gpu.xd, gpu.wp, gpu.ws, gpu.act, list(wl.kseg),
+                                       workspace=work).clone()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        S.segquant_gemm_w8a8_seg(gpu.xd, gpu.wp, gpu.ws, gpu.act, list(wl.kseg), out=out,
+                                 workspace=work)
+    for rep in range(3):
+        out.fill_(7.0)                            # eager work between replays
+        junk = torch.randn(1 << 16, device=DEV).sum()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, y_eager), f"{name}: replay {rep} differs from the eager call"
+        del junk
