@@ -187,20 +187,27 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16 && AMODE != A
   // Lane l of block nb, 32-k sub-block ks of a stage reads 16 bytes of the
   // 1 KiB tile (n-tile nt, k-tile 2u + ks/2) at g*256 + j*16: column
   // j = l % 16 of n-tile 2*nb + (l % 32) / 16, k group g = 2*(ks % 2) + l / 32.
+  // Buffer loads from the wave's first n-tile: the base and the k-tile
+  // offset are wave-uniform (scalar registers), each lane adds a fixed
+  // 32-bit offset, so a load costs no vector address arithmetic.
   const int lane_j = lane & 15, lane_g = lane >> 5;
   const int nt_wave = n0 / 16 + wave * (WN / 16);
-  const int8_t *wcol[NB];
+  const int nt_base = min(nt_wave, NT - 1);
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t *>(a.w + (int64_t)nt_base * KT * 1024), 0, 0x7fffffff, 0x00020000);
+  int woff[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     // n-tiles past N read the last valid tile: those columns are never stored
     const int nt = min(nt_wave + 2 * nb + ((lane & 31) >> 4), NT - 1);
-    wcol[nb] = a.w + (int64_t)nt * KT * 1024 + lane_j * 16 + lane_g * 256;
+    woff[nb] = (nt - nt_base) * KT * 1024 + lane_j * 16 + lane_g * 256;
   }
   v4u wr[2][NB][4];
   auto load_w1 = [&](auto SLOT, int nb, int ks, int u) __attribute__((always_inline)) {
     constexpr int s = decltype(SLOT)::value;
     const int kt = min(2 * u + (ks >> 1), KT - 1);
-    wr[s][nb][ks] = *reinterpret_cast<const v4u *>(wcol[nb] + (int64_t)kt * 1024 + (ks & 1) * 512);
+    wr[s][nb][ks] = __builtin_bit_cast(
+        v4u, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, woff[nb] + (ks & 1) * 512, kt * 1024, 0));
   };
 
   // ---- activation stream: 16-byte pieces, three stages ahead ----
