@@ -18,7 +18,8 @@
 //     instruction.
 //   * Wave w owns output columns [w*BN/4, (w+1)*BN/4) for all BM rows.  The
 //     packed weight (lane-ordered 1 KiB tiles of 64 k x 16 n) gives every
-//     lane its 16-byte piece of a 32x32x32 B operand as one load, so the
+//     lane its 16-byte piece of a 32x32x32 B operand as one buffer load
+//     (wave-uniform base and k offset, a fixed per-lane offset), so the
 //     weight goes from memory straight into registers, never through LDS;
 //     each operand register is refilled with the stage two ahead right after
 //     its last use.  Both polarity halves multiply the same B registers.
@@ -30,7 +31,11 @@
 //     clamp, round half to even) and writes the codes as two int8 planes
 //     (X+, X-), rows padded to 144 bytes so that the 16-byte operand reads
 //     are free of bank conflicts.  Pre-quantised int8 input skips the
-//     arithmetic.
+//     arithmetic.  In the single-segment loop the quantisation of a stage
+//     is spread over all four sub-blocks, one piece beside each twelve
+//     matrix-core instructions.
+//   * Single-scale modes (the W8A8 baseline): one plane of signed codes, one
+//     product per block, the + half's scales only.
 //   * The stage loop is straight-line: prefetch indices are clamped instead
 //     of branched on, K is padded to whole stage pairs with zero codes, and
 //     per-segment values (ends, scales, inverse scales) are read from tables
