@@ -121,6 +121,13 @@ __global__ void calib_finalize_kernel(float *act, int n, int single) {
   act[3 * n + i] = in;
 }
 
+// Each thread owns rows r0 + wave * (64 / L) + sub + j * rows_per_step of the
+// block and, in each, the 8-element chunks col, col + L, ... of the segment.
+// Its (row, chunk) items are taken kBatch at a time, all loads first: the
+// int8 stores may alias the bf16 input as far as the compiler can tell, so
+// one item's store would otherwise hold back the next item's load.
+constexpr int kBatch = 4;
+
 template <bool PLANES>
 __global__ __launch_bounds__(256) void quantize_kernel(ActArgs a) {
   const int seg = blockIdx.y;
@@ -133,29 +140,53 @@ __global__ __launch_bounds__(256) void quantize_kernel(ActArgs a) {
   const int rows_per_step = (64 >> a.lanes_log2) * (blockDim.x >> 6);
   const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
   const int64_t r1 = min(r0 + a.rows_per_block, a.M);
-  for (int64_t r = r0 + wave * (64 >> a.lanes_log2) + sub; r < r1; r += rows_per_step) {
-    const uint16_t *row = a.x + r * a.ld_x;
-    int8_t *qrow = a.q + r * a.ld_q;
-    int64_t k = k0 + 8 * col;
-    for (; k + 8 <= k1; k += 8 * L) {
-      v4u v = load_x8(row + k);
-      if (PLANES) {
-        v2u p, n;
-        quant8_planes(v, inv_pos, inv_neg, p, n);
-        *reinterpret_cast<v2u *>(qrow + k) = p;
-        *reinterpret_cast<v2u *>(qrow + a.plane_stride + k) = n;
-      } else {
-        *reinterpret_cast<v2u *>(qrow + k) = quant8_signed(v, inv_pos, inv_neg);
+  const int64_t rfirst = r0 + wave * (64 >> a.lanes_log2) + sub;
+  const int nrows = rfirst < r1 ? (int)((r1 - rfirst + rows_per_step - 1) / rows_per_step) : 0;
+  const int full = (int)((k1 - k0) / 8);                      // whole chunks in the segment
+  const int nch = col < full ? (full - col + L - 1) / L : 0;  // this lane's chunks per row
+  const int items = nrows * nch;
+  for (int t0 = 0; t0 < items; t0 += kBatch) {
+    v4u v[kBatch];
+    int64_t off[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = min(t0 + u, items - 1);  // past the end: repeat the last item
+      const int j = t / nch, i = t - j * nch;
+      const int64_t r = rfirst + (int64_t)j * rows_per_step;
+      const int64_t k = k0 + 8 * (col + (int64_t)i * L);
+      v[u] = load_x8(a.x + r * a.ld_x + k);
+      off[u] = r * a.ld_q + k;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (t0 + u < items) {
+        if (PLANES) {
+          v2u p, n;
+          quant8_planes(v[u], inv_pos, inv_neg, p, n);
+          *reinterpret_cast<v2u *>(a.q + off[u]) = p;
+          *reinterpret_cast<v2u *>(a.q + a.plane_stride + off[u]) = n;
+        } else {
+          *reinterpret_cast<v2u *>(a.q + off[u]) = quant8_signed(v[u], inv_pos, inv_neg);
+        }
       }
     }
-    for (int64_t kk = k; kk < k1 && kk < k + 8; ++kk) {
-      float f = __uint_as_float(load_bf16(row + kk) << 16);
-      int8_t code = (int8_t)(quant_magic(f, inv_pos, inv_neg) & 0xffu);
-      if (PLANES) {
-        qrow[kk] = code > 0 ? code : 0;
-        qrow[a.plane_stride + kk] = code < 0 ? code : 0;
-      } else {
-        qrow[kk] = code;
+  }
+  // a segment width that is not a multiple of 8: the lane next in turn takes
+  // the last few elements of each of its rows one by one
+  if (k0 + 8 * (int64_t)full < k1 && col == full % L) {
+    for (int j = 0; j < nrows; ++j) {
+      const int64_t r = rfirst + (int64_t)j * rows_per_step;
+      const uint16_t *row = a.x + r * a.ld_x;
+      int8_t *qrow = a.q + r * a.ld_q;
+      for (int64_t kk = k0 + 8 * (int64_t)full; kk < k1; ++kk) {
+        float f = __uint_as_float(load_bf16(row + kk) << 16);
+        int8_t code = (int8_t)(quant_magic(f, inv_pos, inv_neg) & 0xffu);
+        if (PLANES) {
+          qrow[kk] = code > 0 ? code : 0;
+          qrow[a.plane_stride + kk] = code < 0 ? code : 0;
+        } else {
+          qrow[kk] = code;
+        }
       }
     }
   }
@@ -233,8 +264,8 @@ __global__ __launch_bounds__(256) void act_quantize_kernel(ActArgs a) {
 }
 
 // Rows per workgroup and lanes per row for a segment layout: aim for about
-// 16K elements per workgroup on the widest segment.
-void plan_rows(int64_t M, const SegTable &ks, ActArgs &a) {
+// `elems` elements per workgroup on the widest segment.
+void plan_rows(int64_t M, const SegTable &ks, ActArgs &a, int64_t elems = 16384) {
   int64_t wmax = 0;
   for (int i = 0; i < ks.n; ++i) wmax = wmax > ks.end[i] - ks.off[i] ? wmax : ks.end[i] - ks.off[i];
   int64_t chunks = (wmax + 7) / 8;
@@ -242,7 +273,7 @@ void plan_rows(int64_t M, const SegTable &ks, ActArgs &a) {
   while ((1 << lg) < chunks && lg < 6) ++lg;
   a.lanes_log2 = lg;
   int64_t rows_per_step = (64 >> lg) * 4;
-  int64_t rows = (16384 + wmax - 1) / wmax;
+  int64_t rows = (elems + wmax - 1) / wmax;
   rows = ((rows + rows_per_step - 1) / rows_per_step) * rows_per_step;
   if (rows > M) rows = M < 1 ? 1 : M;
   a.rows_per_block = (int32_t)rows;

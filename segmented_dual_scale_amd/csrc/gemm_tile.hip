@@ -55,6 +55,9 @@
 //               sum_i c_i * A_i.  The fp32 sum lives in registers.  (The variant
 //               that dumps accumulators dumps the S_i; a second launch turns
 //               them into the per-segment sums.)
+//   * Tile shapes: 64 x 384 for one K-segment (one workgroup per CU), or
+//     32 x 128 when that would leave most CUs idle (two workgroups per CU);
+//     32 x 256 for STEP, 64 x 256 for MULTI.
 //   * Workgroup -> tile order is XCD-aware: workgroups are dealt to the 8
 //     XCDs round-robin, so XCD x is given one contiguous range of logical
 //     tiles, ordered in groups of 8 row tiles so that the tiles an XCD runs
@@ -72,6 +75,7 @@ namespace {
 
 constexpr int kAPitch = 144;  // bytes per LDS row of one A plane (128 + 16 pad)
 constexpr int kBK = 128;      // K per LDS stage
+constexpr int kSmallTileGrid = 128;  // single segment: below this many 64 x 384 tiles, use 32 x 128
 
 // Activation input: bf16 (quantised here), signed codes, two planes; and the
 // single-scale forms of the first two (one product on the signed code, the
@@ -138,7 +142,7 @@ __device__ __forceinline__ v16i mfma32(const v4u &a, const v4u &b, const v16i &c
 }
 
 template <int BM, int BN, int AMODE, int MODE, bool DEBUG>
-__global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16 && AMODE != A_BF16_1) ? 2 : 1) void gemm_tile_kernel(TileArgs a) {
+__global__ __launch_bounds__(256, (BM == 32 && (MODE == SINGLE || (AMODE != A_BF16 && AMODE != A_BF16_1))) ? 2 : 1) void gemm_tile_kernel(TileArgs a) {
   constexpr int WN = BN / 4;   // columns per wave
   constexpr int MB = BM / 32;  // 32-row blocks
   constexpr int NB = WN / 32;  // 32-column blocks per wave
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(256, (MODE == STEP && AMODE != A_BF16 && AMODE != A
   // start of stage v - XS and quantised during stage v - 1 (XS - 1 stages of
   // memory latency hidden).  Three for the single-segment loop; the fold
   // modes need the registers and keep two.
-  constexpr int XS = MODE == SINGLE ? 3 : 2;
+  constexpr int XS = (MODE == SINGLE && BM == 64) ? 3 : 2;
   constexpr bool SPREAD = spread_quant(MODE, AMODE, XP);
   v4u xr[XS][XP];
   auto load_x = [&](auto SLOT, int u) __attribute__((always_inline)) {
@@ -736,7 +740,15 @@ hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s) {
                                    : p.x ? A_BF16 : (p.q_layout == 1 ? A_PLANES : A_SIGNED);
   const bool debug = p.acc_debug != nullptr;
   // (the tile widths here and in tile_columns() go together)
-  if (p.ks.n == 1) return launch_variant<64, 384, SINGLE>(t, amode, debug, s);
+  if (p.ks.n == 1) {
+    // Fewer 64 x 384 tiles than half the CUs leave the chip mostly idle and
+    // the call latency-bound: 32 x 128 tiles give six times as many
+    // workgroups, two per CU.  (M=64, K=256, N=768 on MI355X: 11.6 us with
+    // two 64 x 384 tiles, 4.7 us with twelve 32 x 128 tiles.)
+    const int64_t big = ((p.M + 63) / 64) * ((p.N + 383) / 384);
+    if (big < kSmallTileGrid) return launch_variant<32, 128, SINGLE>(t, amode, debug, s);
+    return launch_variant<64, 384, SINGLE>(t, amode, debug, s);
+  }
   if (every_step) return launch_variant<32, 256, STEP>(t, amode, debug, s);
   bool even_ends = true;  // every segment end but the last on a whole stage
   for (int i = 0; i + 1 < p.ks.n; ++i) even_ends = even_ends && (p.ks.end[i] % 128 == 0);
