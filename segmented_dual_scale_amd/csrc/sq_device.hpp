@@ -91,9 +91,13 @@ __device__ __forceinline__ v2u quant8_signed(v4u x, float inv_pos, float inv_neg
 }
 
 // Signed codes (4 per dword) -> the - plane (bytes with the sign bit set) and
-// the + plane (the rest).
+// the + plane (the rest).  The byte mask m is 0xff where the sign bit is set:
+// t holds the sign bits, t - (t >> 7) is 0x7f in those bytes (no borrow
+// crosses a byte), and OR-ing t back gives 0xff.  (Full-rate integer ops; a
+// multiply by 0xff would be a quarter-rate instruction.)
 __device__ __forceinline__ void split_signed(uint32_t q, uint32_t &pos, uint32_t &neg) {
-  uint32_t m = ((q >> 7) & 0x01010101u) * 0xffu;
+  const uint32_t t = q & 0x80808080u;
+  const uint32_t m = (t - (t >> 7)) | t;
   neg = q & m;
   pos = q ^ neg;
 }

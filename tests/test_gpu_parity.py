@@ -129,6 +129,9 @@ GEMM_CASES = [
     (130, 704, 64, [64, 128, 512], [32, 32], False, "normal"),
     (64, 256, 768, [256], [256, 256, 256], False, "pos"),
     (64, 256, 256, [128, 128], None, True, "neg"),
+    # one segment on enough 64 x 384 tiles (26 x 5) to use them rather than
+    # the 32 x 128 tiles of small grids: ragged rows, columns and k-tiles
+    (1641, 320, 1904, [320], None, True, "gelu"),
 ]
 
 
@@ -213,6 +216,7 @@ SINGLE_CASES = [
     (130, 704, 64, [64, 128, 512], "normal"),  # tile kernel, a segment ending inside a stage
     (200, 1536, 1536, [64] * 24, "blocks"),    # tile kernel, one k-step per segment; quantise-first
     (300, 512, 2304, [512], "gelu"),           # tile kernel, one segment, quantise-first
+    (1641, 320, 1904, [320], "gelu"),          # tile kernel, one segment on 64 x 384 tiles
 ]
 
 
