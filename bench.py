@@ -504,6 +504,29 @@ def summarize_trace(run_dir: str):
               f"{v[(9 * n) // 10] / 1e3:10.2f}  {name[:150]}")
 
 
+def summarize_pmc(run_dirs, match: str = "gemm_"):
+    """Mean per dispatch of every counter in rocprofv3 --pmc runs (CSV output),
+    per kernel whose name contains `match`."""
+    per = {}
+    for d in run_dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for f in files:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if match not in r["Kernel_Name"]:
+                        continue
+                    k = per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], {})
+                    key = (f, r["Dispatch_Id"])
+                    k[key] = k.get(key, 0.0) + float(r["Counter_Value"])
+    for name in sorted(per):
+        print(name[:150])
+        for c in sorted(per[name]):
+            v = per[name][c]
+            print(f"  {c:32s} {sum(v.values()) / len(v):14.6g}   ({len(v)} dispatches)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -526,12 +549,18 @@ def main():
                          "rocprofv3 --pmc)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print per-kernel duration statistics of a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="print the mean per dispatch of each counter of rocprofv3 --pmc runs, "
+                         "per layer kernel")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the counter record of --workload from two --pmc-pass runs")
     args = ap.parse_args()
 
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
         return
     if args.ingest_pmc:
         import segmented_dual_scale_amd.workloads as W
