@@ -1,0 +1,86 @@
+"""Seeded random layer shapes through the C ABI against the oracle.
+
+The fixed cases elsewhere pin the paths one by one; these draws cover their
+combinations.  Each case draws:
+- M on either side of the kernels' tile edges and of the small-M limit;
+- K in whole 64-wide k-tiles, with a random K-segment layout (boundaries on
+  multiples of 64), sometimes every segment one k-step;
+- N in multiples of 16, with random N-segments of any width, per-column
+  weight scales, or one weight scale per K-segment;
+- an input distribution and an activation input mode.
+
+Bit-exact: the activation scales and every per-segment int32 accumulator (both
+halves).  Within |y - y_ref| <= 8e-3 |y_ref| + 1e-3 max|y_ref|: the bf16 output,
+with and without the accumulator dump.
+"""
+import numpy as np
+import pytest
+
+import segmented_dual_scale_amd as S
+from segmented_dual_scale_amd import workloads as W
+from gpu_common import GpuLayer, OracleLayer, bf16_dev_to_f64, y_tolerance_ok
+
+pytestmark = pytest.mark.gpu
+
+_MS = [1, 2, 3, 5, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 96, 127, 129, 200, 257, 311]
+_KINDS = ["gelu", "silu", "normal", "pos", "neg", "blocks"]
+_MODES = ["bf16", "signed", "planes"]
+
+
+def _draw_cases(n: int = 24, seed: int = 20261203):
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = int(g.choice(_MS))
+        kt = int(g.integers(1, 25))  # k-tiles of 64
+        if kt > 1 and g.random() < 0.2:
+            kseg = [64] * kt  # every segment one k-step
+        else:
+            ns = int(g.integers(1, min(kt, 6) + 1))
+            cuts = sorted(g.choice(np.arange(1, kt), size=ns - 1, replace=False).tolist()) if ns > 1 else []
+            edges = [0] + [64 * c for c in cuts] + [64 * kt]
+            kseg = [b - a for a, b in zip(edges[:-1], edges[1:])]
+        N = 16 * int(g.integers(1, 51))
+        r = g.random()
+        if r < 1 / 3:
+            nseg, per_column = None, True
+        elif r < 2 / 3:
+            nseg, per_column = None, False
+        else:
+            nn = int(g.integers(1, min(N, 5) + 1))
+            cuts = sorted(g.choice(np.arange(1, N), size=nn - 1, replace=False).tolist()) if nn > 1 else []
+            edges = [0] + cuts + [N]
+            nseg, per_column = [b - a for a, b in zip(edges[:-1], edges[1:])], False
+        kind = str(g.choice(_KINDS))
+        mode = str(g.choice(_MODES))
+        cases.append((i, M, 64 * kt, N, kseg, nseg, per_column, kind, mode))
+    return cases
+
+
+CASES = _draw_cases()
+
+
+def _id(c):
+    i, M, K, N, kseg, nseg, per_column, kind, mode = c
+    ns = "col" if per_column else (f"N{len(nseg)}" if nseg else "kseg")
+    return f"{i:02d}_M{M}_K{K}_N{N}_S{len(kseg)}_{ns}_{kind}_{mode}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_id(c) for c in CASES])
+def test_random_shape_parity(case):
+    i, M, K, N, kseg, nseg, per_column, kind, mode = case
+    x, w = W.make_custom(M, K, N, seed=1000 + i, kind=kind, x_scale=2.0)
+    ref = OracleLayer(x, w, kseg, nseg, per_column)
+    gpu = GpuLayer(x, w, kseg, nseg, per_column)
+    assert np.array_equal(gpu.act.cpu().numpy().view(np.uint32), ref.act.view(np.uint32))
+    flag_sets = [S.SEGQ_GEMM_AUTO]
+    if M <= 16:  # both kernels take small M
+        flag_sets.append(S.SEGQ_GEMM_FORCE_TILE)
+    for flags in flag_sets:
+        y, acc = gpu.run(mode, flags=flags, debug=True)
+        assert np.array_equal(acc.cpu().numpy(), ref.acc), f"int32 accumulators, flags {flags}"
+        ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), ref.y)
+        assert ok, f"bf16 Y out of tolerance (flags {flags}): {nbad} elements, worst excess {worst}"
+        y2, _ = gpu.run(mode, flags=flags, debug=False)
+        ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y2), ref.y)
+        assert ok, f"production Y out of tolerance (flags {flags}): {nbad} elements, worst {worst}"
