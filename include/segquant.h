@@ -318,6 +318,27 @@ size_t segquant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t n_
                                      const int32_t *kseg_offset, const int32_t *kseg_width,
                                      uint32_t flags);
 
+/*
+ * segquant_gemm_halves -- which halves a layer needs, from its static scales
+ * ([P1] "SegQuant" notes, DualScale section, and its limitations: the
+ * negative half exists for polarity-asymmetric activations; with no negative
+ * values its term of the reconstruction vanishes).  Host-only: no GPU work.
+ *   act_scales_host  HOST fp32 [4][n_kseg], a copy of the table written by
+ *                    segquant_calibrate_amax (the scales are static, so the
+ *                    copy is taken once, after calibration)
+ * Returns SEGQ_GEMM_SINGLE_SCALE when s_neg and inv_neg are 0 in every
+ * K-segment (the calibration data held no negative value), else 0.  Or'ed
+ * into the flags of segquant_gemm_w8a8_seg with this same table, the layer
+ * then runs one product per element instead of two and, for an input with
+ * no negative elements, gives exactly the DualScale result (the + half's
+ * codes and products are the same; the - half's are all zero).  A negative
+ * element, which DualScale with s_neg = 0 quantises to 0, is instead
+ * quantised with the + half's scale.  On a NULL table or n_kseg outside
+ * [1, SEGQ_MAX_KSEG] returns SEGQ_ERR_NULL or SEGQ_ERR_SEGMENTS and sets
+ * segquant_last_error().
+ */
+int segquant_gemm_halves(const float *act_scales_host, int32_t n_kseg);
+
 /* Which kernel segquant_gemm_w8a8_seg runs for this shape under `flags`
  * (SEGQ_KERNEL_*), or a negative status when the shape is invalid. */
 int segquant_gemm_kernel_for(int64_t M, int64_t N, int64_t K, uint32_t flags);

@@ -32,6 +32,7 @@ __all__ = [
     "SEGQ_GEMM_FORCE_TILE", "SEGQ_GEMM_FORCE_SMALLM", "SEGQ_GEMM_FUSED_QUANT",
     "SEGQ_GEMM_SINGLE_SCALE", "segquant_calibrate_amax_single",
     "SEGQ_ACT_SILU", "SEGQ_ACT_GELU", "segquant_activate_quantize", "SEGQ_GEMM_W4", "SEGQ_KERNEL_TILE", "SEGQ_KERNEL_SMALLM",
+    "segquant_gemm_halves",
 ]
 
 SEGQ_OK = 0
@@ -96,6 +97,7 @@ def load_library():
                                    P, P, ctypes.c_size_t, U32, P],
         "segquant_gemm_workspace_bytes": [I64, I64, I64, I32, P, P, U32],
         "segquant_gemm_kernel_for": [I64, I64, I64, U32],
+        "segquant_gemm_halves": [P, I32],
         "segquant_version": [],
         "segquant_status_string": [ctypes.c_int],
         "segquant_last_error": [],
@@ -167,6 +169,22 @@ def segquant_weight_packed_bytes(K: int, N: int) -> int:
 
 def segquant_gemm_kernel_for(M: int, N: int, K: int, flags: int = SEGQ_GEMM_AUTO) -> int:
     return int(load_library().segquant_gemm_kernel_for(M, N, K, flags))
+
+
+def segquant_gemm_halves(act) -> int:
+    """SEGQ_GEMM_SINGLE_SCALE when the scale table `act` ([4][n_kseg], device
+    or host tensor, or a numpy array) has no negative half, else 0.  A device
+    table is copied to the host (once per layer: the scales are static)."""
+    import numpy as np
+    if hasattr(act, "detach"):
+        act = act.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(act, dtype=np.float32))
+    if a.ndim != 2 or a.shape[0] != 4:
+        raise ValueError(f"scale table of shape {a.shape}, expected [4][n_kseg]")
+    r = load_library().segquant_gemm_halves(a.ctypes.data, a.shape[1])
+    if r < 0:
+        raise SegQuantError(r, "segquant_gemm_halves", segquant_last_error())
+    return int(r)
 
 
 def _calibrate(fn, name, x, kseg, out):

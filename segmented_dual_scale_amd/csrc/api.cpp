@@ -306,6 +306,17 @@ int segquant_gemm_kernel_for(int64_t M, int64_t N, int64_t K, uint32_t flags) {
   return M <= sq::kSmallMMax ? SEGQ_KERNEL_SMALLM : SEGQ_KERNEL_TILE;
 }
 
+int segquant_gemm_halves(const float *act_scales_host, int32_t n_kseg) {
+  if (!act_scales_host) return fail(SEGQ_ERR_NULL, "act_scales_host is NULL");
+  if (n_kseg < 1 || n_kseg > SEGQ_MAX_KSEG)
+    return fail(SEGQ_ERR_SEGMENTS, "K-segment count %d outside [1, %d]", n_kseg, SEGQ_MAX_KSEG);
+  for (int32_t i = 0; i < n_kseg; ++i) {
+    const float s_neg = act_scales_host[n_kseg + i], inv_neg = act_scales_host[3 * n_kseg + i];
+    if (s_neg != 0.0f || inv_neg != 0.0f) return 0;  // the - half carries values: both halves
+  }
+  return (int)SEGQ_GEMM_SINGLE_SCALE;
+}
+
 static bool quantize_first(int kernel, int64_t M, int64_t N, const sq::SegTable &ks,
                            uint32_t flags) {
   return kernel == SEGQ_KERNEL_TILE && !(flags & SEGQ_GEMM_FUSED_QUANT) &&

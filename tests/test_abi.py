@@ -66,6 +66,26 @@ def test_packed_bytes():
     assert S.segquant_weight_packed_bytes(0, 16) == 0
 
 
+def test_gemm_halves_from_host_scales():
+    """One product per element only when no K-segment has a negative half."""
+    a = np.zeros((4, 3), np.float32)
+    a[0] = [0.1, 0.2, 0.3]
+    a[2] = 1.0 / a[0]
+    assert S.segquant_gemm_halves(a) == S.SEGQ_GEMM_SINGLE_SCALE
+    b = a.copy()
+    b[1, 2], b[3, 2] = 0.01, 100.0  # the last segment has negative values
+    assert S.segquant_gemm_halves(b) == 0
+    c = a.copy()
+    c[3, 1] = 5.0  # an inverse without its scale still quantises a - half
+    assert S.segquant_gemm_halves(c) == 0
+    assert lib().segquant_gemm_halves(None, 3) == S.SEGQ_ERR_NULL
+    assert lib().segquant_gemm_halves(a.ctypes.data, 0) == S.SEGQ_ERR_SEGMENTS
+    big = np.zeros((4, 129), np.float32)
+    assert lib().segquant_gemm_halves(big.ctypes.data, 129) == S.SEGQ_ERR_SEGMENTS
+    with pytest.raises(ValueError):
+        S.segquant_gemm_halves(np.zeros((3, 2), np.float32))
+
+
 def test_kernel_choice():
     assert S.segquant_gemm_kernel_for(2, 9216, 1536) == S.SEGQ_KERNEL_SMALLM
     assert S.segquant_gemm_kernel_for(16, 64, 64) == S.SEGQ_KERNEL_SMALLM

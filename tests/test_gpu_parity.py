@@ -260,6 +260,32 @@ def test_single_scale_parity(case, mode):
         assert ok, f"single-scale Y out of tolerance (debug={debug}): {nbad} elements, worst {worst}"
 
 
+@pytest.mark.parametrize("M,K,N,kseg", [(77, 384, 768, [128, 256]), (5, 512, 160, [512]),
+                                         (200, 1536, 1536, [64] * 24)])
+@pytest.mark.parametrize("mode", ["bf16", "signed"])
+def test_halves_choice_on_nonnegative_input(M, K, N, kseg, mode):
+    """A DualScale table with no negative half (calibrated on input >= 0):
+    segquant_gemm_halves picks the one-product GEMM, which then gives the
+    DualScale result exactly: plane 0 equals the oracle's A+ and the oracle's
+    A- is zero; plane 1 untouched; Y within tolerance of the DualScale Y.  On
+    input with negative values the choice is both halves."""
+    import torch
+    x, w = W.make_custom(M, K, N, seed=M + 3 * K + N, kind="pos", x_scale=2.0)
+    ref = OracleLayer(x, w, kseg, None, True)
+    assert not ref.acc[1].any()
+    gpu = GpuLayer(x, w, kseg, None, True)
+    flags = S.segquant_gemm_halves(gpu.act)
+    assert flags == S.SEGQ_GEMM_SINGLE_SCALE
+    y, acc = gpu.run(mode, flags=flags, debug=True)
+    a = acc.cpu().numpy()
+    assert np.array_equal(a[0], ref.acc[0]), "one product differs from the + half's"
+    assert np.all(a[1] == -7), "plane 1 was written"
+    ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), ref.y)
+    assert ok, f"Y out of tolerance: {nbad} elements, worst excess {worst}"
+    xg, _ = W.make_custom(M, K, N, seed=M + 3 * K + N, kind="gelu", x_scale=2.0)
+    assert S.segquant_gemm_halves(S.segquant_calibrate_amax(to_dev_bf16(xg), kseg)) == 0
+
+
 def test_gemm_empty_batch_is_a_noop():
     import torch
     x, w = W.make_custom(4, 128, 32, seed=3)
