@@ -128,38 +128,59 @@ __global__ void calib_finalize_kernel(float *act, int n, int single) {
 // one item's store would otherwise hold back the next item's load.
 constexpr int kBatch = 4;
 
+struct ThreadItems {
+  int64_t rfirst, k0;
+  int rows_per_step, L, col, nrows, nch, items;
+  int full;   // whole 8-element chunks in the segment
+  bool tail;  // this lane also takes the elements past the last whole chunk
+};
+
+__device__ __forceinline__ ThreadItems thread_items(const ActArgs &a, int64_t k0, int64_t k1) {
+  ThreadItems it;
+  it.L = 1 << a.lanes_log2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane >> a.lanes_log2;
+  it.col = lane & (it.L - 1);
+  it.rows_per_step = (64 >> a.lanes_log2) * (blockDim.x >> 6);
+  const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
+  const int64_t r1 = min(r0 + a.rows_per_block, a.M);
+  it.rfirst = r0 + wave * (64 >> a.lanes_log2) + sub;
+  it.nrows = it.rfirst < r1 ? (int)((r1 - it.rfirst + it.rows_per_step - 1) / it.rows_per_step) : 0;
+  it.k0 = k0;
+  it.full = (int)((k1 - k0) / 8);
+  it.nch = it.col < it.full ? (it.full - it.col + it.L - 1) / it.L : 0;
+  it.items = it.nrows * it.nch;
+  it.tail = k0 + 8 * (int64_t)it.full < k1 && it.col == it.full % it.L;
+  return it;
+}
+
+// Row and first column of item t (0 <= t < items).
+__device__ __forceinline__ void item_at(const ThreadItems &it, int t, int64_t &r, int64_t &k) {
+  const int j = t / it.nch, i = t - j * it.nch;
+  r = it.rfirst + (int64_t)j * it.rows_per_step;
+  k = it.k0 + 8 * (it.col + (int64_t)i * it.L);
+}
+
 template <bool PLANES>
 __global__ __launch_bounds__(256) void quantize_kernel(ActArgs a) {
   const int seg = blockIdx.y;
   const int64_t k0 = a.ks.off[seg], k1 = a.ks.end[seg];
   const float inv_pos = a.act[2 * a.n_kseg + seg];
   const float inv_neg = a.single ? inv_pos : a.act[3 * a.n_kseg + seg];
-  const int L = 1 << a.lanes_log2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane >> a.lanes_log2, col = lane & (L - 1);
-  const int rows_per_step = (64 >> a.lanes_log2) * (blockDim.x >> 6);
-  const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
-  const int64_t r1 = min(r0 + a.rows_per_block, a.M);
-  const int64_t rfirst = r0 + wave * (64 >> a.lanes_log2) + sub;
-  const int nrows = rfirst < r1 ? (int)((r1 - rfirst + rows_per_step - 1) / rows_per_step) : 0;
-  const int full = (int)((k1 - k0) / 8);                      // whole chunks in the segment
-  const int nch = col < full ? (full - col + L - 1) / L : 0;  // this lane's chunks per row
-  const int items = nrows * nch;
-  for (int t0 = 0; t0 < items; t0 += kBatch) {
+  const ThreadItems it = thread_items(a, k0, k1);
+  for (int t0 = 0; t0 < it.items; t0 += kBatch) {
     v4u v[kBatch];
     int64_t off[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int t = min(t0 + u, items - 1);  // past the end: repeat the last item
-      const int j = t / nch, i = t - j * nch;
-      const int64_t r = rfirst + (int64_t)j * rows_per_step;
-      const int64_t k = k0 + 8 * (col + (int64_t)i * L);
+      int64_t r, k;
+      item_at(it, min(t0 + u, it.items - 1), r, k);  // past the end: repeat the last item
       v[u] = load_x8(a.x + r * a.ld_x + k);
       off[u] = r * a.ld_q + k;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if (t0 + u < items) {
+      if (t0 + u < it.items) {
         if (PLANES) {
           v2u p, n;
           quant8_planes(v[u], inv_pos, inv_neg, p, n);
@@ -173,12 +194,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(ActArgs a) {
   }
   // a segment width that is not a multiple of 8: the lane next in turn takes
   // the last few elements of each of its rows one by one
-  if (k0 + 8 * (int64_t)full < k1 && col == full % L) {
-    for (int j = 0; j < nrows; ++j) {
-      const int64_t r = rfirst + (int64_t)j * rows_per_step;
+  if (it.tail) {
+    for (int j = 0; j < it.nrows; ++j) {
+      const int64_t r = it.rfirst + (int64_t)j * it.rows_per_step;
       const uint16_t *row = a.x + r * a.ld_x;
       int8_t *qrow = a.q + r * a.ld_q;
-      for (int64_t kk = k0 + 8 * (int64_t)full; kk < k1; ++kk) {
+      for (int64_t kk = k0 + 8 * (int64_t)it.full; kk < k1; ++kk) {
         float f = __uint_as_float(load_bf16(row + kk) << 16);
         int8_t code = (int8_t)(quant_magic(f, inv_pos, inv_neg) & 0xffu);
         if (PLANES) {
@@ -192,15 +213,63 @@ __global__ __launch_bounds__(256) void quantize_kernel(ActArgs a) {
   }
 }
 
+// GELU in its exact form z/2 (1 + erf(z / sqrt 2)), evaluated as
+// z/2 erfc(-z / sqrt 2): the same function, but 1 + erf cancels to nothing in
+// fp32 for z below about -4 while erfc keeps its relative precision.
+// erfc(x), x = |z| / sqrt 2 >= 0, in the form of Numerical Recipes (Press et
+// al., "Numerical Recipes in C", 2nd ed., section 6.2): t exp(-x^2 + P(t)),
+// t = 1 / (1 + x/2), P a degree-9 Chebyshev fit, relative error below 1.2e-7
+// for every x >= 0.  Branch free: erfc(-x) = 2 - erfc(x) gives z >= 0.
+// Rounding x itself would cost about 2 x^2 ulps in the tail, so x enters
+// only t; -x^2 = -z^2/2 is carried as an exact pair (one product and its FMA
+// error), and its product with log2 e is split so that exp2 of the large
+// part sees none of the small part's rounding.  With one-ulp reciprocal and
+// exp2 the result is within 2^-20 of the true value, relative, over the
+// whole bf16 input range (swept on the CPU with those errors injected).
+// Large parts below -120 are evaluated 64 binades up and scaled back
+// exactly, so results in the subnormal range are not flushed.
+__device__ __forceinline__ float gelu_f32(float z) {
+  const float kLog2e = 1.44269504f;             // log2 e, rounded to fp32
+  const float kLog2eLo = 1.92596303e-08f;       // log2 e - kLog2e
+  const float a = fminf(fabsf(z), 20.0f);  // erfc(20 / sqrt 2) underflows: the same result
+  const float x = a * 0.70710678f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, x, 1.0f));
+  float P = __builtin_fmaf(t, 0.17087277f, -0.82215223f);
+  P = __builtin_fmaf(t, P, 1.48851587f);
+  P = __builtin_fmaf(t, P, -1.13520398f);
+  P = __builtin_fmaf(t, P, 0.27886807f);
+  P = __builtin_fmaf(t, P, -0.18628806f);
+  P = __builtin_fmaf(t, P, 0.09678418f);
+  P = __builtin_fmaf(t, P, 0.37409196f);
+  P = __builtin_fmaf(t, P, 1.00002368f);
+  P = __builtin_fmaf(t, P, -1.26551223f);
+  const float p = a * a, e = __builtin_fmaf(a, a, -p);  // z^2 = p + e exactly
+  const float q = -0.5f * p, qe = -0.5f * e;           // -x^2 = q + qe exactly
+  const float hi = q * kLog2e;
+  float lo = __builtin_fmaf(q, kLog2e, -hi);
+  lo = __builtin_fmaf(q, kLog2eLo, lo);
+  lo = __builtin_fmaf(qe + P, kLog2e, lo);
+  const bool deep = hi < -120.0f;
+  const float eh = __builtin_amdgcn_exp2f(deep ? hi + 64.0f : hi) * (deep ? 0x1p-64f : 1.0f);
+  const float E = t * eh * __builtin_amdgcn_exp2f(lo);
+  return 0.5f * z * (z < 0.0f ? E : 2.0f - E);
+}
+
+// SiLU z / (1 + e^-z) as z sigmoid(z), the sigmoid from e^-|z| (library
+// expf): e^-z itself overflows for z below about -88.7, where z / (1 + e^-z)
+// would give 0 while the true value is still a normal float.
+__device__ __forceinline__ float silu_f32(float z) {
+  const float ez = expf(-fabsf(z));
+  const float r = 1.0f / (1.0f + ez);
+  return z * (z >= 0.0f ? r : ez * r);
+}
+
 // Activation of one element in fp32 [P1/P2: the SiLU and GELU outputs whose
-// polarity asymmetry DualScale serves]: SiLU z / (1 + e^-z); GELU in its
-// exact form z/2 (1 + erf(z / sqrt 2)), evaluated as z/2 erfc(-z / sqrt 2)
-// (the same function; 1 + erf cancels to nothing in fp32 for z below about
-// -4, erfc keeps full relative precision).  Library expf / erfcf.
+// polarity asymmetry DualScale serves].
 template <int ACT>
 __device__ __forceinline__ float activate(float z) {
-  if (ACT == 1) return z / (1.0f + expf(-z));
-  return 0.5f * z * erfcf(z * -0.70710678118654752f);
+  if (ACT == 1) return silu_f32(z);
+  return gelu_f32(z);
 }
 
 // Two bf16 pre-activations (one dword) -> two bf16 activations (one dword).
@@ -219,44 +288,52 @@ __global__ __launch_bounds__(256) void act_quantize_kernel(ActArgs a) {
   const int64_t k0 = a.ks.off[seg], k1 = a.ks.end[seg];
   const float inv_pos = WQ ? a.act[2 * a.n_kseg + seg] : 0.0f;
   const float inv_neg = WQ ? (a.single ? inv_pos : a.act[3 * a.n_kseg + seg]) : 0.0f;
-  const int L = 1 << a.lanes_log2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane >> a.lanes_log2, col = lane & (L - 1);
-  const int rows_per_step = (64 >> a.lanes_log2) * (blockDim.x >> 6);
-  const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
-  const int64_t r1 = min(r0 + a.rows_per_block, a.M);
-  for (int64_t r = r0 + wave * (64 >> a.lanes_log2) + sub; r < r1; r += rows_per_step) {
-    const uint16_t *row = a.x + r * a.ld_x;
-    int8_t *qrow = WQ ? a.q + r * a.ld_q : nullptr;
-    uint16_t *xrow = WX ? a.x_out + r * a.ld_xo : nullptr;
-    int64_t k = k0 + 8 * col;
-    for (; k + 8 <= k1; k += 8 * L) {
-      const v4u z = load_x8(row + k);
-      v4u v;
+  const ThreadItems it = thread_items(a, k0, k1);
+  for (int t0 = 0; t0 < it.items; t0 += kBatch) {
+    v4u z[kBatch];
+    int64_t rr[kBatch], kk[kBatch];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = activate2<ACT>(z[j]);
-      if (WX) *reinterpret_cast<v4u *>(xrow + k) = v;
-      if (WQ) {
-        if (PLANES) {
-          v2u p, n;
-          quant8_planes(v, inv_pos, inv_neg, p, n);
-          *reinterpret_cast<v2u *>(qrow + k) = p;
-          *reinterpret_cast<v2u *>(qrow + a.plane_stride + k) = n;
-        } else {
-          *reinterpret_cast<v2u *>(qrow + k) = quant8_signed(v, inv_pos, inv_neg);
+    for (int u = 0; u < kBatch; ++u) {
+      item_at(it, min(t0 + u, it.items - 1), rr[u], kk[u]);  // past the end: repeat the last item
+      z[u] = load_x8(a.x + rr[u] * a.ld_x + kk[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (t0 + u < it.items) {
+        v4u v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = activate2<ACT>(z[u][j]);
+        if (WX) *reinterpret_cast<v4u *>(a.x_out + rr[u] * a.ld_xo + kk[u]) = v;
+        if (WQ) {
+          int8_t *q = a.q + rr[u] * a.ld_q + kk[u];
+          if (PLANES) {
+            v2u p, n;
+            quant8_planes(v, inv_pos, inv_neg, p, n);
+            *reinterpret_cast<v2u *>(q) = p;
+            *reinterpret_cast<v2u *>(q + a.plane_stride) = n;
+          } else {
+            *reinterpret_cast<v2u *>(q) = quant8_signed(v, inv_pos, inv_neg);
+          }
         }
       }
     }
-    for (int64_t kk = k; kk < k1 && kk < k + 8; ++kk) {
-      const uint32_t xb = f32_to_bf16_rne(activate<ACT>(__uint_as_float(load_bf16(row + kk) << 16)));
-      if (WX) xrow[kk] = (uint16_t)xb;
-      if (WQ) {
-        const int8_t code = (int8_t)(quant_magic(__uint_as_float(xb << 16), inv_pos, inv_neg) & 0xffu);
-        if (PLANES) {
-          qrow[kk] = code > 0 ? code : 0;
-          qrow[a.plane_stride + kk] = code < 0 ? code : 0;
-        } else {
-          qrow[kk] = code;
+  }
+  if (it.tail) {  // the elements past the last whole chunk, one by one
+    for (int j = 0; j < it.nrows; ++j) {
+      const int64_t r = it.rfirst + (int64_t)j * it.rows_per_step;
+      const uint16_t *row = a.x + r * a.ld_x;
+      for (int64_t k = k0 + 8 * (int64_t)it.full; k < k1; ++k) {
+        const uint32_t xb = f32_to_bf16_rne(activate<ACT>(__uint_as_float(load_bf16(row + k) << 16)));
+        if (WX) a.x_out[r * a.ld_xo + k] = (uint16_t)xb;
+        if (WQ) {
+          const int8_t code = (int8_t)(quant_magic(__uint_as_float(xb << 16), inv_pos, inv_neg) & 0xffu);
+          int8_t *qrow = a.q + r * a.ld_q;
+          if (PLANES) {
+            qrow[k] = code > 0 ? code : 0;
+            qrow[a.plane_stride + k] = code < 0 ? code : 0;
+          } else {
+            qrow[k] = code;
+          }
         }
       }
     }

@@ -441,6 +441,30 @@ def test_activate_quantize_parity(case, layout):
         assert np.array_equal(gp, qp) and np.array_equal(gn, qn), "fused codes differ"
 
 
+@pytest.mark.parametrize("kind", ["silu", "gelu"])
+def test_activation_every_bf16_input(kind):
+    """Every finite bf16 value (65280 of them, as a 255 x 256 tensor) through
+    the fused activation: each produced bf16 is finite and lies between the
+    bf16 roundings of the fp64 activation minus and plus 2^-19 |act(z)| +
+    2^-140, from the smallest subnormals to the largest magnitudes (where
+    e^-z overflows and erfc underflows)."""
+    import torch
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    z = bits[np.isfinite(W.bf16_bits_to_f32(bits))].reshape(255, 256)
+    act_kind = S.SEGQ_ACT_SILU if kind == "silu" else S.SEGQ_ACT_GELU
+    _, xdev = S.segquant_activate_quantize(to_dev_bf16(z), act_kind, kseg=[256], x_out=True,
+                                           want_codes=False)
+    torch.cuda.synchronize()
+    xf = W.bf16_bits_to_f32(xdev.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.all(np.isfinite(xf))
+    v = oracle.activation(z, kind)
+    delta = 2.0 ** -19 * np.abs(v) + 2.0 ** -140
+    lo = W.bf16_bits_to_f32(W.f32_to_bf16_bits((v - delta).astype(np.float32)))
+    hi = W.bf16_bits_to_f32(W.f32_to_bf16_bits((v + delta).astype(np.float32)))
+    bad = ~((xf >= lo) & (xf <= hi))
+    assert not bad.any(), f"{int(bad.sum())} inputs outside the bound, e.g. z={W.bf16_bits_to_f32(z[bad][:4])}"
+
+
 # ------------------------------------------------------- 4-bit weights ----
 W4_CASES = [
     # M, K, N, kseg, nseg, per_column, kind
