@@ -285,10 +285,13 @@ class Layer:
         self.xs = self.xqs = self.wps = self.ys = self.work = None
 
 
-def measured_peaks(dev, stream):
+def measured_peaks(dev, stream, slab_bytes: int = 0):
     """Ceilings measured on this GPU by the probe library: an int8
     matrix-core-only loop (one wave per SIMD and two), the shader clock while
-    it runs, a streaming read and a device copy of 1 GiB."""
+    it runs, a streaming read and a device copy of 1 GiB, and (slab_bytes > 0)
+    the time per launch of streaming slab_bytes from HBM, launches back to
+    back in a graph over distinct slices of the 1 GiB buffer (so no slice is
+    in a cache), best of several grid sizes."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "segmented_dual_scale_amd", "libsegquant_probe.so")
@@ -344,7 +347,7 @@ def measured_peaks(dev, stream):
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.fill_(1)
     blocks = cus * 8
-    rsink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    rsink = torch.empty(16 * cus * 256, dtype=torch.int32, device=dev)  # also the slab probe's
 
     def read():
         rc = lib.sqprobe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, blocks,
@@ -354,6 +357,35 @@ def measured_peaks(dev, stream):
     with torch.cuda.stream(stream):
         t = timed(read, 5)
     out["hbm_read_gbs"] = nbytes / t / 1e9
+    if slab_bytes > 0:
+        slab = (slab_bytes + 255) // 256 * 256
+        nslab = nbytes // slab
+        best_us, best_blocks = float("inf"), None
+        for blocks in (cus // 2, cus, 2 * cus, 4 * cus, 8 * cus, 16 * cus):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(nslab):
+                    rc = lib.sqprobe_stream_read(ctypes.c_void_p(buf.data_ptr() + i * slab), slab,
+                                                 blocks, ctypes.c_void_p(rsink.data_ptr()), sp)
+                    if rc != 0:
+                        raise RuntimeError(f"sqprobe_stream_read failed ({rc})")
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(5):
+                    g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (5 * nslab)
+            if us < best_us:
+                best_us, best_blocks = us, blocks
+            del g
+        out["hbm_stream_slab_bytes"] = slab
+        out["hbm_stream_slab_us"] = best_us
+        out["hbm_stream_slab_blocks"] = best_blocks
     half = nbytes // 2
     src, dst = buf[:half], buf[half:]
     with torch.cuda.stream(stream):
@@ -363,7 +395,9 @@ def measured_peaks(dev, stream):
                      f"independent accumulators per wave, 4 waves per workgroup, 1 and 2 "
                      f"workgroups per CU ({cus} CUs), clock = shader/constant clock ratio "
                      f"over the loop; grid-stride 16-byte read of 1 GiB; torch copy of 512 MiB; "
-                     f"best of 3-5 timed launches")
+                     f"best of 3-5 timed launches; slab: grid-stride reads of slab_bytes from "
+                     f"{nbytes // max(slab_bytes, 1) if slab_bytes else 0} distinct slices, one launch "
+                     f"each, replayed as a graph, best of {cus // 2}-{16 * cus} workgroups")
     del buf, rsink
     return out
 
@@ -677,10 +711,15 @@ def main():
     if not args.no_producer:
         line["producer_fusion"] = producer_fusion(S, W, dev, stream)
     if not args.no_peaks:
-        mp = measured_peaks(dev, stream)
+        slab = (wl.K * wl.N // (2 if args.mode == "w4" else 1)) if roof["bound"] == "hbm" else 0  # the weight one call streams
+        mp = measured_peaks(dev, stream, slab)
         line["measured_peaks"] = mp
         ref = mp["hbm_read_gbs"] if roof["bound"] == "hbm" else mp["int8_mfma_tops"]
         roof["frac_of_measured"] = roof["achieved"] / ref
+        if slab:
+            # a launch that only streams this call's weight, back to back
+            roof["stream_floor_us"] = mp["hbm_stream_slab_us"]
+            roof["over_stream_floor"] = roof["per_launch"]["avg_us"] / mp["hbm_stream_slab_us"]
         for v in line.get("all_workloads", {}).values():
             ref = mp["hbm_read_gbs"] if v["bound"] == "hbm" else mp["int8_mfma_tops"]
             v["frac_of_measured"] = v["value"] / ref
