@@ -118,6 +118,11 @@ GEMM_CASES = [
     (8, 512, 112, [128, 384], None, True, "blocks"),   # largest M with both halves in one operand
     (5, 2048, 64, [64] * 32, [64], False, "blocks"),    # 32 segments, the full weight ring
     (9, 1024, 160, [1024], [160], False, "gelu"),       # smallest M with an operand per half
+    # one K-segment, M <= 8, the streaming kernel's rings of 16, 32 and 32
+    # slots (10, 25 and 32 k-tiles), odd numbers of n-tiles
+    (8, 640, 48, [640], None, True, "gelu"),
+    (3, 1600, 80, [1600], [80], False, "silu"),
+    (1, 2048, 32, [2048], None, True, "normal"),
     (40, 320, 96, [320], None, True, "gelu"),           # one segment, odd number of k-tiles
     (70, 192, 400, [192], [400], False, "silu"),        # one segment, three k-tiles, ragged N
     (16, 640, 256, [64] * 10, [256], False, "blocks"),
