@@ -553,3 +553,73 @@ def test_graph_replays_match_eager(name):
         torch.cuda.synchronize()
         assert torch.equal(out, y_eager), f"{name}: replay {rep} differs from the eager call"
         del junk
+
+
+def _replay_matches(run, out, y_eager, what):
+    """Capture run() in a graph; replay three times with eager work and
+    synchronisations between replays; every replay equals y_eager."""
+    import torch
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        run()
+    for rep in range(3):
+        out.fill_(7)                              # eager work between replays
+        junk = torch.randn(1 << 16, device=DEV).sum()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, y_eager), f"{what}: replay {rep} differs from the eager call"
+        del junk
+
+
+@pytest.mark.parametrize("name", ["c2_adanorm_gemv", "c3_dit_ffn_fc2"])
+@pytest.mark.parametrize("variant", ["single", "w4"])
+def test_graph_replays_of_variants(name, variant):
+    """The single-scale layer and the W4A8 layer (on c3: the widening launch
+    into the workspace, then the GEMM) captured and replayed: every replay
+    equals the eager call bit for bit."""
+    import torch
+    wl, x, w = W.make_inputs(name)
+    nseg = None if wl.per_column else list(wl.nseg)
+    kseg = list(wl.kseg)
+    xd = to_dev_bf16(x)
+    if variant == "single":
+        act = S.segquant_calibrate_amax_single(xd, kseg)
+        wp, ws = S.segquant_quantize_weight(to_dev(w), kseg, nseg, wl.per_column)
+        flags = S.SEGQ_GEMM_SINGLE_SCALE
+    else:
+        act = S.segquant_calibrate_amax(xd, kseg)
+        wp, ws = S.segquant_quantize_weight(to_dev(w), kseg, nseg, wl.per_column, bits=4)
+        flags = S.SEGQ_GEMM_W4
+    nb = S.segquant_gemm_workspace_bytes(wl.M, wl.N, wl.K, kseg, flags=flags)
+    work = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV) if nb else None
+    out = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=DEV)
+    y_eager = S.segquant_gemm_w8a8_seg(xd, wp, ws, act, kseg, workspace=work, flags=flags).clone()
+    torch.cuda.synchronize()
+    _replay_matches(lambda: S.segquant_gemm_w8a8_seg(xd, wp, ws, act, kseg, out=out,
+                                                     workspace=work, flags=flags),
+                    out, y_eager, f"{name} {variant}")
+
+
+@pytest.mark.parametrize("layout", ["signed", "planes"])
+def test_graph_replays_of_activation_quantise(layout):
+    """The fused GELU + dual-scale quantisation captured and replayed: the
+    codes of every replay equal the eager call's."""
+    import torch
+    M, K, kseg = 600, 1536, [512, 1024]
+    z, _ = W.make_custom(M, K, 16, seed=11, kind="normal", x_scale=2.0)
+    zd = to_dev_bf16(z)
+    lay = S.SEGQ_Q_SIGNED if layout == "signed" else S.SEGQ_Q_PLANES
+    _, xdev = S.segquant_activate_quantize(zd, S.SEGQ_ACT_GELU, kseg=kseg, x_out=True,
+                                           want_codes=False)
+    act = S.segquant_calibrate_amax(xdev, kseg)
+    q_eager, _ = S.segquant_activate_quantize(zd, S.SEGQ_ACT_GELU, act, kseg, lay)
+    q_eager = q_eager.clone()
+    out = torch.empty_like(q_eager)
+    torch.cuda.synchronize()
+    _replay_matches(lambda: S.segquant_activate_quantize(zd, S.SEGQ_ACT_GELU, act, kseg, lay,
+                                                         out=out),
+                    out, q_eager, f"activation quantise {layout}")
+
