@@ -311,9 +311,14 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
     xr[i] = *reinterpret_cast<const v4u *>(src);
     if (QL == 1) xn[QL == 1 ? i : 0] = *reinterpret_cast<const v4u *>(src + a.plane_stride);
     if (QL < 0) {
-      const int sg = __builtin_popcount(a.fold_mask & ((1u << (c >> 3)) - 1u));
-      ipv[QL < 0 ? i : 0] = a.act[2 * nS + sg];
-      inv_[QL < 0 ? i : 0] = a.act[(a.single ? 2 : 3) * nS + sg];
+      if (SEG1 && i > 0) {  // one K-segment: every piece has the same pair, loaded once
+        ipv[QL < 0 ? i : 0] = ipv[0];
+        inv_[QL < 0 ? i : 0] = inv_[0];
+      } else {
+        const int sg = SEG1 ? 0 : __builtin_popcount(a.fold_mask & ((1u << (c >> 3)) - 1u));
+        ipv[QL < 0 ? i : 0] = a.act[2 * nS + sg];
+        inv_[QL < 0 ? i : 0] = a.act[(a.single ? 2 : 3) * nS + sg];
+      }
     }
   }
 
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   for (int i = 0; i < kStreamXR; ++i) {
     pin_load(xr[i]);
     if (QL == 1) pin_load(xn[QL == 1 ? i : 0]);
-    if (QL < 0) {
+    if (QL < 0 && !(SEG1 && i > 0)) {
       pin_load(ipv[QL < 0 ? i : 0]);
       pin_load(inv_[QL < 0 ? i : 0]);
     }
