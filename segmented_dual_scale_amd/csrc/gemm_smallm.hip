@@ -282,7 +282,12 @@ struct StreamArgs {
 // fold needs no data from other lanes.  Otherwise each half has its own A
 // operand (rows at or past M zero).
 // W4: 4-bit weight tiles (512 bytes, 8 per lane), widened in registers.
-template <int QL, int RING, bool SEG1, bool PACK, bool W4, bool DEBUG>
+// XR: 16-byte activation pieces staged per thread (up to XR * 256 pieces):
+// every slot is loaded, before the weight stream, whether a thread has a
+// piece there or not (a branch around the loads would break the
+// straight-line load order the chain's waits rely on), so calls with few
+// pieces take XR = 2 and issue six loads per thread fewer.
+template <int QL, int RING, bool SEG1, bool PACK, bool W4, bool DEBUG, int XR>
 __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t planes[2 * kSmallMMax * kStreamPitch];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -301,10 +306,10 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   //     ends before it).  Pieces past the end load a valid piece and are
   //     never stored.  These go first: what is issued after the weight
   //     stream waits behind it.
-  v4u xr[kStreamXR], xn[QL == 1 ? kStreamXR : 1];
-  float ipv[QL < 0 ? kStreamXR : 1], inv_[QL < 0 ? kStreamXR : 1];
+  v4u xr[XR], xn[QL == 1 ? XR : 1];
+  float ipv[QL < 0 ? XR : 1], inv_[QL < 0 ? XR : 1];
 #pragma unroll
-  for (int i = 0; i < kStreamXR; ++i) {
+  for (int i = 0; i < XR; ++i) {
     const int pc = min(tid + i * kStreamThreads, a.pieces - 1);
     const int row = (int)__umulhi((uint32_t)pc, a.ppr_magic), c = pc - row * a.pieces_per_row;
     const uint8_t *src = a.x + row * a.ld_bytes + c * 16;
@@ -330,7 +335,8 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   const float sn_l = a.act[(a.single ? 0 : nS) + ti];
   float wsp[kStreamPre];
 #pragma unroll
-  for (int j = 0; j < kStreamPre; ++j) wsp[j] = a.w_scale[(int64_t)min(j, nS - 1) * a.N + n];
+  for (int j = 0; j < kStreamPre; ++j)  // (one K-segment: one scale, loaded once)
+    wsp[j] = SEG1 && j > 0 ? wsp[0] : a.w_scale[(int64_t)min(j, nS - 1) * a.N + n];
 
   // (3) the whole weight stream of this wave (the scheduling barriers keep
   //     the loads above ahead of it in issue order)
@@ -348,7 +354,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   }
 
 #pragma unroll
-  for (int i = 0; i < kStreamXR; ++i) {
+  for (int i = 0; i < XR; ++i) {
     pin_load(xr[i]);
     if (QL == 1) pin_load(xn[QL == 1 ? i : 0]);
     if (QL < 0 && !(SEG1 && i > 0)) {
@@ -359,11 +365,11 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   pin_load(sp_l);
   pin_load(sn_l);
 #pragma unroll
-  for (int j = 0; j < kStreamPre; ++j) pin_load(wsp[j]);
+  for (int j = 0; j < (SEG1 ? 1 : kStreamPre); ++j) pin_load(wsp[j]);
 
   // (4) quantise (or split) X into the two planes
 #pragma unroll
-  for (int i = 0; i < kStreamXR; ++i) {
+  for (int i = 0; i < XR; ++i) {
     const int p = tid + i * kStreamThreads;
     if (p < a.pieces) {
       const int row = (int)__umulhi((uint32_t)p, a.ppr_magic), c = p - row * a.pieces_per_row;
@@ -543,10 +549,10 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_smallm_kernel(StreamArgs 
   }
 }
 
-template <int RING, bool SEG1, bool PACK, bool W4>
+template <int RING, bool SEG1, bool PACK, bool W4, int XR>
 void launch_stream_ring(const StreamArgs &a, int ql, bool debug, dim3 grid, hipStream_t s) {
 #define SQ_STREAM(QLV, DBG)                                                           \
-  hipLaunchKernelGGL((gemm_smallm_kernel<QLV, RING, SEG1, PACK, W4, DBG>), grid,      \
+  hipLaunchKernelGGL((gemm_smallm_kernel<QLV, RING, SEG1, PACK, W4, DBG, XR>), grid,  \
                      dim3(kStreamThreads), 0, s, a)
   if (debug) {
     if (ql < 0) SQ_STREAM(-1, true);
@@ -563,12 +569,15 @@ void launch_stream_ring(const StreamArgs &a, int ql, bool debug, dim3 grid, hipS
 template <int RING, bool W4>
 void launch_stream_w(const StreamArgs &a, int ql, bool debug, dim3 grid, hipStream_t s) {
   const bool pack = a.M <= 8;
+  const bool few = a.pieces <= 2 * kStreamThreads;  // (M <= 8 only: XR = 2)
   if (a.n_kseg == 1) {
-    if (pack) launch_stream_ring<RING, true, true, W4>(a, ql, debug, grid, s);
-    else launch_stream_ring<RING, true, false, W4>(a, ql, debug, grid, s);
+    if (pack && few) launch_stream_ring<RING, true, true, W4, 2>(a, ql, debug, grid, s);
+    else if (pack) launch_stream_ring<RING, true, true, W4, kStreamXR>(a, ql, debug, grid, s);
+    else launch_stream_ring<RING, true, false, W4, kStreamXR>(a, ql, debug, grid, s);
   } else {
-    if (pack) launch_stream_ring<RING, false, true, W4>(a, ql, debug, grid, s);
-    else launch_stream_ring<RING, false, false, W4>(a, ql, debug, grid, s);
+    if (pack && few) launch_stream_ring<RING, false, true, W4, 2>(a, ql, debug, grid, s);
+    else if (pack) launch_stream_ring<RING, false, true, W4, kStreamXR>(a, ql, debug, grid, s);
+    else launch_stream_ring<RING, false, false, W4, kStreamXR>(a, ql, debug, grid, s);
   }
 }
 
