@@ -33,6 +33,8 @@ ACT_CASES = [
     (129, 1536, [1536], "silu"),
     (64, 1000, [512, 488], "gelu"),      # ragged K (last segment not 64-aligned)
     (5, 8200, [4096, 4104], "normal"),
+    (70, 600, [64] * 9 + [24], "blocks"),   # ten segments, the last one 24 wide
+    (2, 65600, [8192] * 8 + [64], "normal"),  # long rows, nine segments
     (17, 256, [256], "pos"),
     (17, 256, [256], "neg"),
 ]
