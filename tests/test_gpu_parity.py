@@ -295,14 +295,18 @@ def test_halves_choice_on_nonnegative_input(M, K, N, kseg, mode):
 
 @pytest.mark.parametrize("M", [2, 40])
 @pytest.mark.parametrize("mode", ["bf16", "signed"])
-def test_gemm_at_the_int32_bound(M, mode):
-    """One K-segment of 132096 (the largest multiple of 64 within
-    SEGQ_MAX_KSEG_WIDTH), with operands that put every accumulator at its
-    largest magnitude: rows of -1 quantise to -128 throughout, rows of +1 to
-    127, columns of -0.02 / +0.02 to -127 / 127, so A- reaches 132096 * 128 *
-    127 = 2147352576 (2^31 - 131072).  The chunked small-M kernel (M = 2) and
-    the tile kernel (M = 40): accumulators bit-exact, Y within tolerance."""
+@pytest.mark.parametrize("nk", [1, 4])
+def test_gemm_at_the_int32_bound(M, mode, nk):
+    """K = 132096 (the largest multiple of 64 within SEGQ_MAX_KSEG_WIDTH) in
+    one K-segment, or four (the tile kernel's int32 running sums then span
+    all of K), with operands that put every accumulator at its largest
+    magnitude: rows of -1 quantise to -128 throughout, rows of +1 to 127,
+    columns of -0.02 / +0.02 to -127 / 127, so one segment's A- reaches
+    132096 * 128 * 127 = 2147352576 (2^31 - 131072).  The chunked small-M
+    kernel (M = 2) and the tile kernel (M = 40): accumulators bit-exact, Y
+    within tolerance."""
     K, N = 132096, 32
+    kseg = [K // nk] * nk
     x = np.ones((M, K), np.float32)
     x[0::2] = -1.0
     g = np.random.default_rng(7)
@@ -312,9 +316,9 @@ def test_gemm_at_the_int32_bound(M, mode):
     w[:, 0::2] = -0.02
     w[:, 8:12] = (g.standard_normal((K, 4)) * 0.02).astype(np.float32)
     xb = W.f32_to_bf16_bits(x)
-    ref = OracleLayer(xb, w, [K], None, True)
-    assert int(np.abs(ref.acc.astype(np.int64)).max()) == K * 128 * 127
-    gpu = GpuLayer(xb, w, [K], None, True)
+    ref = OracleLayer(xb, w, kseg, None, True)
+    assert int(np.abs(ref.acc.astype(np.int64)).max()) == (K // nk) * 128 * 127
+    gpu = GpuLayer(xb, w, kseg, None, True)
     y, acc = gpu.run(mode, debug=True)
     assert np.array_equal(acc.cpu().numpy(), ref.acc)
     ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), ref.y)
