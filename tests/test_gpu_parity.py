@@ -325,6 +325,40 @@ def test_gemm_at_the_int32_bound(M, mode, nk):
     assert ok, f"Y out of tolerance: {nbad} elements, worst excess {worst}"
 
 
+@pytest.mark.parametrize("M", [3, 40])
+@pytest.mark.parametrize("mode", ["bf16", "signed", "planes"])
+@pytest.mark.parametrize("case", ["x_zero", "w_zero", "one_segment_zero", "one_group_zero"])
+def test_gemm_zero_ranges(M, mode, case):
+    """Zero ranges (s = 0 and inv = 0, so that half or group is all zero
+    codes): an all-zero activation or weight gives Y = 0 exactly; a zero
+    K-segment of X, or a zero weight group, contributes nothing beside the
+    others.  Scales and accumulators bit-exact, Y within tolerance (exact
+    zeros where the whole output is zero)."""
+    K, N, kseg, nseg = 512, 96, [128, 256, 128], [32, 32, 32]
+    x, w = W.make_custom(M, K, N, seed=M + len(case), kind="gelu", x_scale=2.0)
+    xf = W.bf16_bits_to_f32(x)
+    if case == "x_zero":
+        xf[:] = 0.0
+    elif case == "one_segment_zero":
+        xf[:, 128:384] = 0.0
+    elif case == "w_zero":
+        w[:] = 0.0
+    else:
+        w[128:384, 32:64] = 0.0  # K-segment 1 x N-segment 1: one weight group
+    x = W.f32_to_bf16_bits(xf)
+    ref = OracleLayer(x, w, kseg, nseg, False)
+    gpu = GpuLayer(x, w, kseg, nseg, False)
+    assert np.array_equal(gpu.act.cpu().numpy().view(np.uint32), ref.act.view(np.uint32))
+    assert np.array_equal(gpu.ws.cpu().numpy().view(np.uint32), ref.ws.view(np.uint32))
+    y, acc = gpu.run(mode, debug=True)
+    assert np.array_equal(acc.cpu().numpy(), ref.acc)
+    yg = bf16_dev_to_f64(y)
+    if case in ("x_zero", "w_zero"):
+        assert not ref.y.any() and not yg.any(), "the output is not exactly zero"
+    ok, worst, nbad = y_tolerance_ok(yg, ref.y)
+    assert ok, f"Y out of tolerance: {nbad} elements, worst excess {worst}"
+
+
 def test_gemm_empty_batch_is_a_noop():
     import torch
     x, w = W.make_custom(4, 128, 32, seed=3)
