@@ -387,6 +387,44 @@ def test_gemm_does_not_write_outside_its_rows():
         assert ok
 
 
+@pytest.mark.parametrize("M,K,N,kseg", [(3, 512, 160, [512]),            # streaming small-M
+                                         (5, 4096, 64, [2048, 2048]),     # chunked small-M
+                                         (77, 384, 272, [128, 256]),      # tile, fused
+                                         (150, 512, 2304, [512])])        # tile, quantise-first
+@pytest.mark.parametrize("mode", ["bf16", "signed", "planes"])
+def test_gemm_padded_operands_and_guard_bands(M, K, N, kseg, mode):
+    """X (or its codes) inside a padded buffer (ld_x = K + 72, ld_q = K +
+    48) and Y inside a larger one (rows above and below, 24 columns to the
+    right): the result equals the oracle's (accumulators bit-exact) and no
+    byte of Y's buffer outside the M x N window changes."""
+    import torch
+    x, w = W.make_custom(M, K, N, seed=M + K, kind="gelu", x_scale=2.0)
+    ref = OracleLayer(x, w, kseg, None, True)
+    gpu = GpuLayer(x, w, kseg, None, True)
+    xpad = np.zeros((M, K + 72), np.uint16)
+    xpad[:, :K] = x
+    xd = to_dev_bf16(xpad)[:, :K]
+    big = torch.full((M + 5, N + 24), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = big[2:M + 2, :N]
+    acc = torch.full((2, len(kseg), M, N), -7, dtype=torch.int32, device=DEV)
+    if mode == "bf16":
+        S.segquant_gemm_w8a8_seg(xd, gpu.wp, gpu.ws, gpu.act, kseg, out=out, acc_debug=acc)
+    else:
+        lay = S.SEGQ_Q_SIGNED if mode == "signed" else S.SEGQ_Q_PLANES
+        ldq = K + 48
+        qbuf = torch.zeros((M, ldq) if mode == "signed" else (2, M, ldq), dtype=torch.int8,
+                           device=DEV)
+        S.segquant_quantize_dualscale(xd, gpu.act, kseg, lay, out=qbuf)
+        S.segquant_gemm_w8a8_seg(None, gpu.wp, gpu.ws, gpu.act, kseg, N=N, xq=qbuf, q_layout=lay,
+                                 out=out, acc_debug=acc)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref.acc)
+    b = big.float().cpu().numpy()
+    assert np.all(b[:2] == 7.0) and np.all(b[M + 2:] == 7.0) and np.all(b[:, N:] == 7.0)
+    ok, worst, nbad = y_tolerance_ok(b[2:M + 2, :N].astype(np.float64), ref.y)
+    assert ok, f"Y out of tolerance: {nbad} elements, worst excess {worst}"
+
+
 # ------------------------------------------- full-size named workloads ----
 @pytest.mark.parametrize("name", W.ORDER)
 def test_full_size_workload(name):
