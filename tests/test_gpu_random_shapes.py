@@ -27,7 +27,7 @@ _KINDS = ["gelu", "silu", "normal", "pos", "neg", "blocks"]
 _MODES = ["bf16", "signed", "planes"]
 
 
-def _draw_cases(n: int = 24, seed: int = 20261203):
+def _draw_cases(n: int = 48, seed: int = 20261203):
     g = np.random.default_rng(seed)
     cases = []
     for i in range(n):
