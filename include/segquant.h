@@ -29,8 +29,10 @@
  *
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
- *     never allocates or frees device memory, keeps no pointer after the
- *     call returns, and needs no workspace.
+ *     never allocates or frees device memory and keeps no pointer after the
+ *     call returns.  The only scratch memory is the optional, caller-owned
+ *     workspace of segquant_gemm_w8a8_seg (its size from
+ *     segquant_gemm_workspace_bytes).
  *   - Segment lists are HOST arrays (offset[n], width[n]), read only during
  *     the call: offsets start at 0, are contiguous, widths are positive and
  *     sum to the segmented dimension.  Every K-segment boundary except the
