@@ -214,13 +214,35 @@ class Layer:
                                      out=self.ys[j])
 
     def time(self, stream, steps: int, warmup: int, use_graph: bool, min_seconds: float = 0.0):
-        """Average ms per step over >= `steps` timed steps (whole graph replays)."""
+        """Average ms per step.  min_seconds == 0: exactly `steps` timed steps,
+        one graph of `steps` calls over the rotating sets, replayed once
+        untimed and then once timed.  min_seconds > 0 (the summary of all
+        workloads): whole replays of a graph of one call per set, as many as
+        fill min_seconds (and at least `steps` steps)."""
         import torch
         R = self.R
         with torch.cuda.stream(stream):
             for i in range(max(warmup, R)):
                 self.step(i)
         torch.cuda.synchronize()
+        if use_graph and min_seconds <= 0:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(steps):
+                    self.step(i)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                graph.replay()
+            torch.cuda.synchronize()
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                start.record(stream)
+                graph.replay()
+                end.record(stream)
+            torch.cuda.synchronize()
+            del graph
+            return start.elapsed_time(end) / steps, steps
         graph = None
         if use_graph:
             graph = torch.cuda.CUDAGraph()
