@@ -703,6 +703,12 @@ def main():
                              "frac": mm["frac"], "us_per_step": ms * 1e3, "steps": n,
                              "kernel": lay.kernel, "launches_per_step": lay.launches,
                              "M": lay.wl.M, "K": lay.wl.K, "N": lay.wl.N}
+            if not args.no_cpu_baseline:  # the oracle on a bounded row sample, about 1 s
+                cb = cpu_baseline(lay.wl, lay.x, lay.w, seconds=1.0)
+                summary[name]["cpu_oracle"] = {
+                    "value": cb["value"], "unit": cb["unit"], "cores": cb["cores"],
+                    "rows": int(cb["sample"].split(" of ")[0]),
+                    "gpu_over_cpu": mm["value"] / cb["value"]}
             if lay.launches == 2:
                 gms = lay.gemm_ms(stream, 1, 10, use_graph, min_seconds=0.05)
                 summary[name]["gemm_us_per_launch"] = gms * 1e3
