@@ -16,8 +16,9 @@
  *        CVPR 2026).
  *   [P2] "SegQuant", project page (hliangzhao.me/works/segquant.html).
  *
- * Readings taken where the pages leave a step open (each is listed, with its
- * reason, in the design notes of the repository):
+ * Readings taken where the pages leave a step open (the reason for each is
+ * that it is the plainest reading the rest of the pages support, or the one
+ * that keeps the codes in int8; each is pinned by a test):
  *   R1  q_max = 127 and q_min = 128 (a magnitude): s+ = max/127,
  *       s- = |min|/128, so the negative half lives in [-128, 0].
  *   R2  "round" is round-half-to-even.
