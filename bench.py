@@ -113,6 +113,99 @@ def read_traffic(kernel: str, workload: str, mode: str):
             "record": os.path.relpath(path, ROOT)}
 
 
+def trace_record_path(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"trace_{kernel}_{workload}.txt")
+
+
+def read_trace(kernel: str, workload: str, mode: str):
+    """Per-dispatch duration statistics of the kernel from the committed
+    rocprofv3 kernel-trace record, or None when there is none for the current
+    kernel source."""
+    path = trace_record_path(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ln.startswith("#") or ":" not in ln:
+                continue
+            k, v = ln.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != source_digest(kernel) or rec.get("mode") != mode:
+        return None
+    out = {k: float(rec[k]) for k in ("calls", "mean_us", "p10_us", "median_us", "p90_us")}
+    out["calls"] = int(out["calls"])
+    out["record"] = os.path.relpath(path, ROOT)
+    return out
+
+
+def _trace_spans(run_dir: str):
+    """{kernel name: [(start, end) ns, in start order]} of a kernel-trace run."""
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {run_dir}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                per.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    for v in per.values():
+        v.sort()
+    return per
+
+
+def _trace_durations(run_dir: str):
+    return {k: [e - s for s, e in v] for k, v in _trace_spans(run_dir).items()}
+
+
+def _stats_us(v):
+    v = sorted(v)
+    n = len(v)
+    return {"calls": n, "mean_us": sum(v) / n / 1e3, "p10_us": v[n // 10] / 1e3,
+            "median_us": v[n // 2] / 1e3, "p90_us": v[(9 * n) // 10] / 1e3}
+
+
+def ingest_trace(run_dir: str, workload: str, mode: str, kernel: str, command: str,
+                 timed: int):
+    """Write the kernel-trace record of the layer kernel on one workload from
+    a rocprofv3 --kernel-trace run of the headline phase alone.  The record's
+    statistics cover the timed replay: the last `timed` dispatches of the
+    kernel in start order (the benchmark replays its graph of `steps` calls
+    once untimed, then once timed, after eager warm-up calls)."""
+    spans = _trace_spans(run_dir)
+    mine = sorted(sp for name, v in spans.items() if kernel in name for sp in v)
+    if len(mine) < timed:
+        raise SystemExit(f"{len(mine)} dispatches of {kernel} in {run_dir}, fewer than {timed}")
+    last = mine[-timed:]
+    st = _stats_us([e - s for s, e in last])
+    gaps = [last[i + 1][0] - last[i][1] for i in range(len(last) - 1)]
+    allst = _stats_us([e - s for s, e in mine])
+    path = trace_record_path(kernel, workload)
+    with open(path, "w") as fh:
+        fh.write(f"# Dispatch durations (End - Start) of {kernel} on {workload} ({mode}\n"
+                 f"# activation input), from a rocprofv3 kernel trace of the benchmark's\n"
+                 f"# headline phase alone (no other workload, no single-scale launches):\n"
+                 f"#   {command}\n"
+                 f"# The statistics are those of the timed replay: the last {timed} dispatches\n"
+                 f"# of the kernel.  The tracer inserts gaps between dispatches (mean\n"
+                 f"# {sum(gaps) / max(1, len(gaps)) / 1e3:.2f} us here); the benchmark's own event\n"
+                 f"# timing of the same replay without the tracer includes the real gaps.\n"
+                 f"# All {allst['calls']} dispatches of the run (eager warm-up included): mean\n"
+                 f"# {allst['mean_us']:.2f} us, median {allst['median_us']:.2f} us.\n"
+                 f"# source_sha256 covers {', '.join(KERNEL_SOURCES[kernel])}.\n")
+        fh.write(f"kernel: {kernel}\nworkload: {workload}\nmode: {mode}\n")
+        fh.write(f"source_sha256: {source_digest(kernel)}\n")
+        for k in ("calls", "mean_us", "p10_us", "median_us", "p90_us"):
+            fh.write(f"{k}: {st[k]:.4f}\n" if k != "calls" else f"{k}: {st[k]}\n")
+        fh.write("# every kernel of the run (all dispatches):\n")
+        for name, v in sorted(spans.items(), key=lambda kv: -sum(e - s for s, e in kv[1])):
+            s2 = _stats_us([e - s for s, e in v])
+            fh.write(f"#   {s2['calls']:6d} calls  mean {s2['mean_us']:9.2f} us  median "
+                     f"{s2['median_us']:9.2f} us  {name[:120]}\n")
+    print(open(path).read())
+
+
 def cpu_baseline(wl, x, w, seconds: float = 12.0):
     """The oracle, as it stands, on a bounded row sample of the workload."""
     import numpy as np
@@ -141,11 +234,15 @@ def cpu_baseline(wl, x, w, seconds: float = 12.0):
         value, unit = alg_bytes(sub) / t / 1e9, "GB/s"
     else:
         value, unit = alg_ops(sub) / t / 1e12, "TOPS"
-    return {"value": value, "unit": unit, "cores": min(threads, rows), "kind": "oracle",
+    used = min(threads, rows)  # the oracle parallelises over rows only
+    host = len(os.sched_getaffinity(0))
+    return {"value": value, "unit": unit, "cores": used, "threads_used": used,
+            "host_cores": host, "kind": "oracle",
             "sample": f"{rows} of {wl.M} rows (full K={wl.K}, N={wl.N}), median of {len(times)} "
                       f"calls of oracle_dualscale_linear (quantise, exact int32 products, fp64 "
-                      f"dequantise) over {sum(times):.1f} s; calibration and weight "
-                      f"quantisation not timed",
+                      f"dequantise) over {sum(times):.1f} s on {used} of the {host} host cores "
+                      f"this process may use (OpenMP over rows: at most one thread per row); "
+                      f"calibration and weight quantisation not timed",
             "seconds_per_call": t}
 
 
@@ -543,15 +640,7 @@ def ingest_pmc(fetch_dir: str, write_dir: str, workload: str, mode: str, kernel:
 
 def summarize_trace(run_dir: str):
     """Per-kernel duration statistics of a rocprofv3 --kernel-trace run (CSV output)."""
-    files = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no kernel_trace.csv under {run_dir}")
-    per = {}
-    for f in files:
-        with open(f) as fh:
-            for r in csv.DictReader(fh):
-                per.setdefault(r["Kernel_Name"], []).append(
-                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    per = _trace_durations(run_dir)
     print(f"{'calls':>7} {'mean_us':>10} {'p10_us':>10} {'median_us':>10} {'p90_us':>10}  kernel")
     for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         v.sort()
@@ -610,6 +699,12 @@ def main():
                          "per layer kernel")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the counter record of --workload from two --pmc-pass runs")
+    ap.add_argument("--ingest-trace", metavar="DIR",
+                    help="write the kernel-trace record of --workload from a rocprofv3 "
+                         "--kernel-trace run of the headline phase (--no-all --no-producer "
+                         "--no-peaks --no-cpu-baseline)")
+    ap.add_argument("--trace-command", default=None,
+                    help="the traced command, for the record written by --ingest-trace")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -617,6 +712,13 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
+        return
+    if args.ingest_trace:
+        import segmented_dual_scale_amd.workloads as W
+        wl = W.WORKLOADS[args.workload]
+        kernel = "gemm_smallm_kernel" if wl.M <= 16 else "gemm_tile_kernel"
+        cmd = args.trace_command or "(command not given)"
+        ingest_trace(args.ingest_trace, args.workload, args.mode, kernel, cmd, args.steps)
         return
     if args.ingest_pmc:
         import segmented_dual_scale_amd.workloads as W
@@ -669,6 +771,12 @@ def main():
             "frac": mk["frac"], "traffic": None, "kernel": layer.kernel,
             "per_launch": {"alg_bytes": layer.alg_bytes(), "alg_int8_ops": alg_ops(wl),
                            "avg_us": ms_kernel * 1e3}}
+    tt = read_trace(layer.kernel, wl.name, args.mode)
+    if tt is not None:
+        # the same kernel's dispatch durations under rocprofv3 (its own run)
+        tt["frac_from_mean"] = layer.metrics(tt["mean_us"] * 1e-3)["frac"]
+        tt["frac_from_median"] = layer.metrics(tt["median_us"] * 1e-3)["frac"]
+        roof["trace"] = tt
     tr = read_traffic(layer.kernel, wl.name, args.mode)
     if tr is not None:
         roof["traffic"] = tr["bytes_per_launch"]

@@ -23,6 +23,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "segquant_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# SEGQUANT_ORACLE_LIBRARY names another build of the same source (the
+# sanitizer test builds one with address and undefined-behaviour checks).
+_LIB_OVERRIDE = os.environ.get("SEGQUANT_ORACLE_LIBRARY")
 
 _lib = None
 
@@ -43,9 +46,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     I32 = ctypes.c_int32

@@ -58,7 +58,10 @@ SEGQ_KERNEL_TILE = 1
 SEGQ_KERNEL_SMALLM = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsegquant.so")
+# SEGQUANT_LIBRARY names another build of the same library (the tests use it
+# for a build whose host code carries address and undefined-behaviour
+# sanitizers); by default the in-tree build is loaded.
+_LIB_PATH = os.environ.get("SEGQUANT_LIBRARY") or os.path.join(_HERE, "libsegquant.so")
 _lib = None
 
 

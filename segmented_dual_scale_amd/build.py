@@ -41,36 +41,43 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
+def object_path(src: str) -> str:
+    return os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+
+
+def compile_source(src: str, out: str | None = None, extra_flags=None, verbose: bool = False) -> str:
+    """Compile one source of csrc/ to an object file (default: _build/<name>.o)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    hipcc = _hipcc()
-    flags = CFLAGS + list(extra_flags or [])
+    obj = out or object_path(src)
+    cmd = [_hipcc(), *CFLAGS, *(extra_flags or []), "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    if verbose and r.stderr.strip():
+        print(r.stderr, file=sys.stderr)
+    return obj
 
-    def compile_one(src: str) -> str:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
-        if verbose and r.stderr.strip():
-            print(r.stderr, file=sys.stderr)
-        return obj
 
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(PROBE_SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+def link_shared(out: str, objs, extra_flags=None) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *(extra_flags or []), "-o", tmp,
+           *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
 
-    def link(out, parts):
-        tmp = out + ".tmp%d" % os.getpid()
-        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *parts]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-        os.replace(tmp, out)
 
-    link(OUT, objs[:len(SOURCES)])
-    link(PROBE_OUT, objs[len(SOURCES):])
+def build(verbose: bool = False, extra_flags=None) -> str:
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda f: compile_source(f, extra_flags=extra_flags, verbose=verbose),
+                           srcs))
+    link_shared(OUT, objs[:len(SOURCES)])
+    link_shared(PROBE_OUT, objs[len(SOURCES):])
     return OUT
 
 

@@ -73,29 +73,37 @@ class GpuLayer:
         del wd
         torch.cuda.synchronize()
 
-    def run(self, mode="bf16", flags=S.SEGQ_GEMM_AUTO, debug=False, workspace="auto"):
+    def run(self, mode="bf16", flags=S.SEGQ_GEMM_AUTO, debug=False, workspace="auto", out=None):
         import torch
         acc = None
         if debug:
             acc = torch.full((2, len(self.kseg), self.M, self.N), -7, dtype=torch.int32, device=DEV)
         if mode == "bf16":
             y = S.segquant_gemm_w8a8_seg(self.xd, self.wp, self.ws, self.act, self.kseg,
-                                         acc_debug=acc, workspace=workspace, flags=flags)
+                                         acc_debug=acc, workspace=workspace, flags=flags, out=out)
         else:
             layout = S.SEGQ_Q_SIGNED if mode == "signed" else S.SEGQ_Q_PLANES
             xq = S.segquant_quantize_dualscale(self.xd, self.act, self.kseg, layout)
             y = S.segquant_gemm_w8a8_seg(None, self.wp, self.ws, self.act, self.kseg, xq=xq,
-                                         q_layout=layout, N=self.N, acc_debug=acc, flags=flags)
+                                         q_layout=layout, N=self.N, acc_debug=acc, flags=flags,
+                                         out=out)
         torch.cuda.synchronize()
         return y, acc
 
 
-def sample_rows(M: int, n_random: int, seed: int = 0) -> np.ndarray:
-    """First rows, the last rows (ragged tail of the row tiles) and random
-    rows in between, sorted and unique."""
+def rows_every_block(M: int, block: int = 32, seed: int = 0) -> np.ndarray:
+    """The first and last 8 rows and one random row of every `block`-row
+    block, sorted and unique.  Every row tile of the large-M kernels is a
+    whole number of 32-row blocks, so each tile has a sampled row."""
     g = np.random.default_rng(seed)
     rows = set(range(min(8, M))) | set(range(max(0, M - 8), M))
-    if M > 16:
-        rows |= set(int(r) for r in g.choice(np.arange(8, M - 8), size=min(n_random, M - 16),
-                                             replace=False))
+    for b0 in range(0, M, block):
+        rows.add(int(g.integers(b0, min(M, b0 + block))))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def nan_filled_bf16(M: int, N: int):
+    """A bf16 [M][N] device tensor holding a NaN in every element: an output
+    element that a call leaves unwritten keeps it."""
+    import torch
+    return torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)

@@ -100,3 +100,35 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_trace_record_written_and_read_back(tmp_path, monkeypatch, capsys):
+    """--ingest-trace keeps only the layer kernel's dispatches; the bench reads
+    the record back only for the current kernel source and mode."""
+    B = _bench()
+    monkeypatch.setattr(B, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    tdir = tmp_path / "trace"
+    tdir.mkdir()
+    kernel, wl = "gemm_smallm_kernel", "c2_adanorm_gemv"
+    with open(tdir / "run_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        # five warm-up dispatches of 50 us, then the timed ten of 1..10 us
+        for i in range(5):
+            w.writerow([f"void sq::{kernel}<1>(args)", 1000 * i, 1000 * i + 50_000])
+        for i in range(10):
+            t0 = 10_000_000 + 100_000 * i
+            w.writerow([f"void sq::{kernel}<1>(args)", t0, t0 + 1000 * (i + 1)])
+        w.writerow(["sqprobe_stream_read", 0, 99_000])
+    B.ingest_trace(str(tdir), wl, "bf16", kernel, "python3 bench.py --no-all", 10)
+    capsys.readouterr()
+    t = B.read_trace(kernel, wl, "bf16")
+    assert t["calls"] == 10
+    assert t["mean_us"] == pytest.approx(5.5)
+    assert t["median_us"] == pytest.approx(6.0) and t["p10_us"] == pytest.approx(2.0)
+    assert t["p90_us"] == pytest.approx(10.0)
+    assert B.read_trace(kernel, wl, "signed") is None
+    path = tmp_path / "profiles" / f"trace_{kernel}_{wl}.txt"
+    path.write_text(path.read_text().replace(B.source_digest(kernel), "0" * 64))
+    assert B.read_trace(kernel, wl, "bf16") is None

@@ -10,8 +10,8 @@ import pytest
 import oracle
 import segmented_dual_scale_amd as S
 from segmented_dual_scale_amd import workloads as W
-from gpu_common import (DEV, GpuLayer, OracleLayer, bf16_dev_to_f64, sample_rows, to_dev,
-                        to_dev_bf16, y_tolerance_ok)
+from gpu_common import (DEV, GpuLayer, OracleLayer, bf16_dev_to_f64, nan_filled_bf16,
+                        rows_every_block, to_dev, to_dev_bf16, y_tolerance_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -429,12 +429,14 @@ def test_gemm_padded_operands_and_guard_bands(M, K, N, kseg, mode):
 @pytest.mark.parametrize("name", W.ORDER)
 def test_full_size_workload(name):
     """At the workloads' full sizes and in the configuration the benchmark
-    times: scales, packed weights bit-exact; int32 accumulators and Y on
-    sampled rows (first, last -- the ragged row tile -- and random)."""
+    times: scales, packed weights bit-exact; int32 accumulators and Y on the
+    first and last 8 rows and one random row of every 32-row block (so every
+    row tile of the kernel, the ragged last one included); Y prefilled with
+    NaN, so an element of the whole M x N output that no tile writes fails."""
     import torch
     wl, x, w = W.make_inputs(name)
     nseg = None if wl.per_column else list(wl.nseg)
-    rows = sample_rows(wl.M, 24) if wl.M > 64 else np.arange(wl.M)
+    rows = rows_every_block(wl.M) if wl.M > 64 else np.arange(wl.M)
     ref = OracleLayer(x, w, wl.kseg, nseg, wl.per_column, rows=rows, with_acc=True)
     gpu = GpuLayer(x, w, wl.kseg, nseg, wl.per_column)
     assert np.array_equal(gpu.act.cpu().numpy().view(np.uint32), ref.act.view(np.uint32))
@@ -445,10 +447,13 @@ def test_full_size_workload(name):
     # as the benchmark calls it (a workspace when the library asks for one),
     # and the fused launch
     for flags in (S.SEGQ_GEMM_AUTO, S.SEGQ_GEMM_FUSED_QUANT):
-        y, _ = gpu.run("bf16", debug=False, flags=flags)
+        y, _ = gpu.run("bf16", debug=False, flags=flags, out=nan_filled_bf16(wl.M, wl.N))
+        assert not bool(torch.isnan(y).any()), f"{name} flags {flags}: output elements left unwritten"
         ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y)[rows], ref.y, ymax)
         assert ok, f"{name} flags {flags}: {nbad} sampled outputs out of tolerance, worst {worst}"
-        yd, acc = gpu.run("bf16", debug=True, flags=flags)
+        yd, acc = gpu.run("bf16", debug=True, flags=flags, out=nan_filled_bf16(wl.M, wl.N))
+        assert not bool(torch.isnan(yd).any()), \
+            f"{name} flags {flags}: accumulator-dumping variant left output elements unwritten"
         acc_rows = acc.index_select(2, ridx).cpu().numpy()
         del acc
         assert np.array_equal(acc_rows, ref.acc), f"{name} flags {flags}: int32 accumulators differ"
