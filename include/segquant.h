@@ -308,6 +308,35 @@ int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
                            uint32_t flags, void *stream);
 
 /*
+ * segquant_gemm_w8a8_seg_noalloc -- segquant_gemm_w8a8_seg without a
+ * workspace and without any device allocation, for callers that cannot
+ * allocate: code under stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Arguments, validation, results and errors are those of
+ * segquant_gemm_w8a8_seg (same kernels, bit-identical outputs), less the
+ * workspace.
+ *
+ * What the ordinary call would use a workspace for (the quantise-first int8
+ * codes, M*K bytes; the int8 widening of 4-bit weights, K*N bytes) comes from
+ * a device array of SEGQ_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends (its address is looked up on
+ * the first call on each device).  Quantise-first codes that would not fit
+ * are replaced by the fused launch (same codes and products); a required
+ * widening that does not fit is refused with SEGQ_ERR_UNSUPPORTED before any
+ * HIP call.  All calls on one GPU share its array: calls that overlap on one
+ * GPU race, so order them (one stream).  The call makes no hipMalloc or
+ * hipFree and calls no allocating library routine.
+ */
+#define SEGQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+int segquant_gemm_w8a8_seg_noalloc(int64_t M, int64_t N, int64_t K,
+                                   const uint16_t *x_bf16, int64_t ld_x,
+                                   const int8_t *xq, int64_t ld_q, int32_t q_layout,
+                                   const int8_t *w_packed, const float *w_scale,
+                                   int32_t n_kseg, const int32_t *kseg_offset,
+                                   const int32_t *kseg_width, const float *act_scales,
+                                   uint16_t *y_bf16, int64_t ld_y, int32_t *acc_debug,
+                                   uint32_t flags, void *stream);
+
+/*
  * segquant_gemm_workspace_bytes -- the workspace with which
  * segquant_gemm_w8a8_seg, given bf16 input of this shape and these
  * K-segments, quantises first (M * K bytes), or 0 when it quantises inside

@@ -32,7 +32,7 @@ __all__ = [
     "SEGQ_GEMM_FORCE_TILE", "SEGQ_GEMM_FORCE_SMALLM", "SEGQ_GEMM_FUSED_QUANT",
     "SEGQ_GEMM_SINGLE_SCALE", "segquant_calibrate_amax_single",
     "SEGQ_ACT_SILU", "SEGQ_ACT_GELU", "segquant_activate_quantize", "SEGQ_GEMM_W4", "SEGQ_KERNEL_TILE", "SEGQ_KERNEL_SMALLM",
-    "segquant_gemm_halves",
+    "segquant_gemm_halves", "segquant_gemm_w8a8_seg_noalloc", "SEGQ_NOALLOC_SCRATCH_BYTES",
 ]
 
 SEGQ_OK = 0
@@ -56,6 +56,7 @@ SEGQ_ACT_SILU = 1
 SEGQ_ACT_GELU = 2
 SEGQ_KERNEL_TILE = 1
 SEGQ_KERNEL_SMALLM = 2
+SEGQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # SEGQUANT_LIBRARY names another build of the same library (the tests use it
@@ -98,6 +99,8 @@ def load_library():
         "segquant_weight_packed_bytes_w4": [I64, I64],
         "segquant_gemm_w8a8_seg": [I64, I64, I64, P, I64, P, I64, I32, P, P, I32, P, P, P, P, I64,
                                    P, P, ctypes.c_size_t, U32, P],
+        "segquant_gemm_w8a8_seg_noalloc": [I64, I64, I64, P, I64, P, I64, I32, P, P, I32, P, P,
+                                           P, P, I64, P, U32, P],
         "segquant_gemm_workspace_bytes": [I64, I64, I64, I32, P, P, U32],
         "segquant_gemm_kernel_for": [I64, I64, I64, U32],
         "segquant_gemm_halves": [P, I32],
@@ -356,4 +359,35 @@ def segquant_gemm_w8a8_seg(x, w_packed, w_scale, act_scales, kseg: Optional[Sequ
                                       _ptr(acc_debug), _ptr(workspace), ws_bytes, flags,
                                       _stream(src)),
            "segquant_gemm_w8a8_seg")
+    return out
+
+
+def segquant_gemm_w8a8_seg_noalloc(x, w_packed, w_scale, act_scales, out,
+                                   kseg: Optional[Sequence[int]] = None, N: Optional[int] = None,
+                                   xq=None, q_layout: int = SEGQ_Q_SIGNED, acc_debug=None,
+                                   flags: int = SEGQ_GEMM_AUTO):
+    """segquant_gemm_w8a8_seg through its no-allocation entry point: no
+    workspace, no device allocation in the call (the library's own scratch
+    array stands in for the workspace).  `out` (bf16 [M][N]) is required:
+    this path allocates nothing, here or in the library."""
+    lib = load_library()
+    src = x if x is not None else xq
+    if x is not None:
+        M, K = x.shape
+        ld_x, ld_q = _ld(x, "x"), 0
+    else:
+        M = xq.shape[-2]
+        if kseg is None:
+            raise ValueError("kseg is required with a pre-quantised input")
+        K = sum(kseg)
+        ld_x, ld_q = 0, xq.stride(-2)
+    if N is None:
+        N = w_scale.shape[1]
+    off, wid = _segs(kseg, K)
+    _check(lib.segquant_gemm_w8a8_seg_noalloc(M, N, K, _ptr(x), ld_x, _ptr(xq), ld_q, q_layout,
+                                              _ptr(w_packed), _ptr(w_scale), len(wid),
+                                              _arr_ptr(off), _arr_ptr(wid), _ptr(act_scales),
+                                              _ptr(out), _ld(out, "out"), _ptr(acc_debug), flags,
+                                              _stream(src)),
+           "segquant_gemm_w8a8_seg_noalloc")
     return out

@@ -13,20 +13,26 @@
 #include <string>
 
 #include "../../include/segquant.h"
+#include "sq_api.hpp"
 #include "sq_launch.hpp"
 
 namespace {
 
 thread_local std::string g_err;
 
-int fail(int status, const char *fmt, ...) {
+int vfail(int status, const char *fmt, va_list ap) {
   char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
   g_err = buf;
   return status;
+}
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int r = vfail(status, fmt, ap);
+  va_end(ap);
+  return r;
 }
 
 int ok() {
@@ -106,6 +112,118 @@ int hip_status(hipError_t e, const char *what) {
 }
 
 }  // namespace
+
+namespace sq {
+
+int api_fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int r = vfail(status, fmt, ap);
+  va_end(ap);
+  return r;
+}
+
+int api_hip_status(hipError_t e, const char *what) { return hip_status(e, what); }
+
+static int gemm_check_shape(int64_t M, int64_t N, int64_t K, uint32_t flags);
+
+int gemm_validate(const GemmCall &c, SegTable &ks) {
+  int st = gemm_check_shape(c.M, c.N, c.K, c.flags);
+  if (st) return st;
+  if (c.M > 0) {
+    if ((c.x != nullptr) == (c.xq != nullptr))
+      return fail(SEGQ_ERR_NULL, "exactly one of x_bf16 and xq must be given");
+    if (c.x) {
+      if ((st = check_x(c.x, c.M, c.K, c.ld_x))) return st;
+    } else {
+      if (c.q_layout != SEGQ_Q_SIGNED && c.q_layout != SEGQ_Q_PLANES)
+        return fail(SEGQ_ERR_SHAPE, "unknown q_layout %d", c.q_layout);
+      if (c.q_layout == SEGQ_Q_PLANES && (c.flags & SEGQ_GEMM_SINGLE_SCALE))
+        return fail(SEGQ_ERR_UNSUPPORTED, "the single-scale product takes bf16 or signed-code input");
+      if (c.ld_q < c.K)
+        return fail(SEGQ_ERR_SHAPE, "ld_q %lld < K %lld", (long long)c.ld_q, (long long)c.K);
+      if (c.ld_q % 16 != 0)
+        return fail(SEGQ_ERR_ALIGN, "ld_q %lld is not a multiple of 16", (long long)c.ld_q);
+      if (!aligned16(c.xq)) return fail(SEGQ_ERR_ALIGN, "xq is not 16-byte aligned");
+    }
+    if (!c.w_packed || !c.w_scale || !c.act || !c.y)
+      return fail(SEGQ_ERR_NULL, "w_packed, w_scale, act_scales or y_bf16 is NULL");
+    if (!aligned16(c.w_packed)) return fail(SEGQ_ERR_ALIGN, "w_packed is not 16-byte aligned");
+    if (c.ld_y < c.N)
+      return fail(SEGQ_ERR_SHAPE, "ld_y %lld < N %lld", (long long)c.ld_y, (long long)c.N);
+    if ((reinterpret_cast<uintptr_t>(c.y) & 1u) ||
+        (c.acc && (reinterpret_cast<uintptr_t>(c.acc) & 3u)))
+      return fail(SEGQ_ERR_ALIGN, "y_bf16 or acc_debug is misaligned");
+  }
+  if ((st = read_kseg(c.n_kseg, c.kseg_offset, c.kseg_width, c.K, SEGQ_MAX_KSEG_WIDTH, ks)))
+    return st;
+  if (ks.n > 1 && c.K > SEGQ_MAX_KSEG_WIDTH)
+    return fail(SEGQ_ERR_UNSUPPORTED,
+                "with several K-segments K must be <= %d (int32 running sums over all of K); K=%lld",
+                SEGQ_MAX_KSEG_WIDTH, (long long)c.K);
+  return ok();
+}
+
+static bool quantize_first(int kernel, int64_t M, int64_t N, const sq::SegTable &ks,
+                           uint32_t flags);
+static size_t w4_widen_bytes(int kernel, int64_t M, int64_t N, int64_t K, const sq::SegTable &ks,
+                             uint32_t flags, bool bf16_input);
+
+size_t gemm_workspace_need(const GemmCall &c, const SegTable &ks, uint32_t flags) {
+  const int kernel = segquant_gemm_kernel_for(c.M, c.N, c.K, flags);
+  return w4_widen_bytes(kernel, c.M, c.N, c.K, ks, flags, c.x != nullptr) +
+         (c.x && quantize_first(kernel, c.M, c.N, ks, flags) ? (size_t)(c.M * c.K) : 0);
+}
+
+int gemm_enqueue(const GemmCall &c, const SegTable &ks, void *workspace, size_t workspace_bytes) {
+  if (c.M == 0) return ok();
+  const int64_t M = c.M, N = c.N, K = c.K;
+  const uint32_t flags = c.flags;
+  sq::GemmProblem p{};
+  p.M = M; p.N = N; p.K = K;
+  p.x = c.x; p.ld_x = c.ld_x;
+  p.xq = c.xq; p.ld_q = c.ld_q; p.q_layout = c.q_layout;
+  p.w_packed = c.w_packed; p.w_scale = c.w_scale; p.act = c.act;
+  p.ks = ks;
+  p.y = c.y; p.ld_y = c.ld_y; p.acc_debug = c.acc;
+  p.single_scale = (flags & SEGQ_GEMM_SINGLE_SCALE) != 0;
+  hipStream_t stream = (hipStream_t)c.stream;
+  const int kernel = segquant_gemm_kernel_for(M, N, K, flags);
+  // 4-bit weights: the streaming small-M kernel reads them as they are;
+  // every other path first widens them to int8 tiles in the workspace
+  const size_t widen = w4_widen_bytes(kernel, M, N, K, ks, flags, c.x != nullptr);
+  if (widen && (!workspace || workspace_bytes < widen))
+    return fail(SEGQ_ERR_UNSUPPORTED,
+                "4-bit weights on this shape need a workspace of at least %zu bytes "
+                "(segquant_gemm_workspace_bytes)", widen);
+  p.w4 = (flags & SEGQ_GEMM_W4) && !widen;
+  if (widen) {
+    int8_t *w8 = static_cast<int8_t *>(workspace);
+    hipError_t e = sq::launch_widen_w4(c.w_packed, K, N, w8, stream);
+    if (e != hipSuccess) return hip_status(e, "widen launch");
+    p.w_packed = w8;
+  }
+  uint8_t *ws_rest = workspace ? static_cast<uint8_t *>(workspace) + widen : nullptr;
+  const size_t ws_rest_bytes = workspace ? workspace_bytes - widen : 0;
+  if (c.x && ws_rest && quantize_first(kernel, M, N, ks, flags) &&
+      ws_rest_bytes >= (size_t)(M * K)) {
+    // quantise once into the workspace, then the GEMM from the signed codes
+    int8_t *codes = reinterpret_cast<int8_t *>(ws_rest);
+    hipError_t e = sq::launch_quantize(c.x, M, K, c.ld_x, ks, c.act, codes, K, SEGQ_Q_SIGNED,
+                                       p.single_scale, stream);
+    if (e != hipSuccess) return hip_status(e, "quantize launch");
+    p.x = nullptr;
+    p.ld_x = 0;
+    p.xq = codes;
+    p.ld_q = K;
+    p.q_layout = SEGQ_Q_SIGNED;
+  }
+  hipError_t e = kernel == SEGQ_KERNEL_SMALLM ? sq::launch_gemm_smallm(p, stream)
+                                              : sq::launch_gemm_tile(p, stream);
+  return hip_status(e, "gemm launch");
+}
+
+}  // namespace sq
 
 extern "C" {
 
@@ -280,7 +398,10 @@ int segquant_unpack_weight_w4(const int8_t *w_packed, int64_t K, int64_t N, int8
   return unpack_weight(w_packed, K, N, w_kn, ld_w, true, stream);
 }
 
-static int gemm_check(int64_t M, int64_t N, int64_t K, uint32_t flags) {
+}  // extern "C"
+
+namespace sq {
+static int gemm_check_shape(int64_t M, int64_t N, int64_t K, uint32_t flags) {
   if (M < 0 || N < 1 || K < 1 || M > kI32Max || N > kI32Max || K > kI32Max)
     return fail(SEGQ_ERR_SHAPE, "bad shape M=%lld N=%lld K=%lld", (long long)M, (long long)N,
                 (long long)K);
@@ -297,9 +418,12 @@ static int gemm_check(int64_t M, int64_t N, int64_t K, uint32_t flags) {
                 (long long)M);
   return SEGQ_OK;
 }
+}  // namespace sq
+
+extern "C" {
 
 int segquant_gemm_kernel_for(int64_t M, int64_t N, int64_t K, uint32_t flags) {
-  int st = gemm_check(M, N, K, flags);
+  int st = sq::gemm_check_shape(M, N, K, flags);
   if (st) return st;
   if (flags & SEGQ_GEMM_FORCE_TILE) return SEGQ_KERNEL_TILE;
   if (flags & SEGQ_GEMM_FORCE_SMALLM) return SEGQ_KERNEL_SMALLM;
@@ -317,6 +441,9 @@ int segquant_gemm_halves(const float *act_scales_host, int32_t n_kseg) {
   return (int)SEGQ_GEMM_SINGLE_SCALE;
 }
 
+}  // extern "C"
+
+namespace sq {
 static bool quantize_first(int kernel, int64_t M, int64_t N, const sq::SegTable &ks,
                            uint32_t flags) {
   return kernel == SEGQ_KERNEL_TILE && !(flags & SEGQ_GEMM_FUSED_QUANT) &&
@@ -331,17 +458,20 @@ static size_t w4_widen_bytes(int kernel, int64_t M, int64_t N, int64_t K, const 
   if (kernel == SEGQ_KERNEL_SMALLM && sq::smallm_reads_w4(M, K, ks.n, bf16_input)) return 0;
   return (size_t)K * (size_t)N;
 }
+}  // namespace sq
+
+extern "C" {
 
 size_t segquant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t n_kseg,
                                      const int32_t *kseg_offset, const int32_t *kseg_width,
                                      uint32_t flags) {
-  if (gemm_check(M, N, K, flags)) return 0;
+  if (sq::gemm_check_shape(M, N, K, flags)) return 0;
   sq::SegTable ks{};
   if (read_kseg(n_kseg, kseg_offset, kseg_width, K, SEGQ_MAX_KSEG_WIDTH, ks)) return 0;
   ok();
   const int kernel = segquant_gemm_kernel_for(M, N, K, flags);
-  return w4_widen_bytes(kernel, M, N, K, ks, flags, true) +
-         (quantize_first(kernel, M, N, ks, flags) ? (size_t)(M * K) : 0);
+  return sq::w4_widen_bytes(kernel, M, N, K, ks, flags, true) +
+         (sq::quantize_first(kernel, M, N, ks, flags) ? (size_t)(M * K) : 0);
 }
 
 int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
@@ -353,81 +483,16 @@ int segquant_gemm_w8a8_seg(int64_t M, int64_t N, int64_t K,
                            uint16_t *y_bf16, int64_t ld_y, int32_t *acc_debug,
                            void *workspace, size_t workspace_bytes,
                            uint32_t flags, void *stream) {
-  int st = gemm_check(M, N, K, flags);
-  if (st) return st;
-  if (M > 0) {
-    if ((x_bf16 != nullptr) == (xq != nullptr))
-      return fail(SEGQ_ERR_NULL, "exactly one of x_bf16 and xq must be given");
-    if (x_bf16) {
-      if ((st = check_x(x_bf16, M, K, ld_x))) return st;
-    } else {
-      if (q_layout != SEGQ_Q_SIGNED && q_layout != SEGQ_Q_PLANES)
-        return fail(SEGQ_ERR_SHAPE, "unknown q_layout %d", q_layout);
-      if (q_layout == SEGQ_Q_PLANES && (flags & SEGQ_GEMM_SINGLE_SCALE))
-        return fail(SEGQ_ERR_UNSUPPORTED, "the single-scale product takes bf16 or signed-code input");
-      if (ld_q < K) return fail(SEGQ_ERR_SHAPE, "ld_q %lld < K %lld", (long long)ld_q, (long long)K);
-      if (ld_q % 16 != 0)
-        return fail(SEGQ_ERR_ALIGN, "ld_q %lld is not a multiple of 16", (long long)ld_q);
-      if (!aligned16(xq)) return fail(SEGQ_ERR_ALIGN, "xq is not 16-byte aligned");
-    }
-    if (!w_packed || !w_scale || !act_scales || !y_bf16)
-      return fail(SEGQ_ERR_NULL, "w_packed, w_scale, act_scales or y_bf16 is NULL");
-    if (!aligned16(w_packed)) return fail(SEGQ_ERR_ALIGN, "w_packed is not 16-byte aligned");
-    if (ld_y < N) return fail(SEGQ_ERR_SHAPE, "ld_y %lld < N %lld", (long long)ld_y, (long long)N);
-    if ((reinterpret_cast<uintptr_t>(y_bf16) & 1u) ||
-        (acc_debug && (reinterpret_cast<uintptr_t>(acc_debug) & 3u)))
-      return fail(SEGQ_ERR_ALIGN, "y_bf16 or acc_debug is misaligned");
-    if (workspace && !aligned16(workspace))
-      return fail(SEGQ_ERR_ALIGN, "workspace is not 16-byte aligned");
-  }
+  const sq::GemmCall c{M,       N,          K,        x_bf16,      ld_x,        xq,
+                       ld_q,    q_layout,   w_packed, w_scale,     n_kseg,      kseg_offset,
+                       kseg_width, act_scales, y_bf16, ld_y,     acc_debug,   flags,
+                       stream};
+  if (workspace && !aligned16(workspace))
+    return fail(SEGQ_ERR_ALIGN, "workspace is not 16-byte aligned");
   sq::SegTable ks{};
-  if ((st = read_kseg(n_kseg, kseg_offset, kseg_width, K, SEGQ_MAX_KSEG_WIDTH, ks))) return st;
-  if (ks.n > 1 && K > SEGQ_MAX_KSEG_WIDTH)
-    return fail(SEGQ_ERR_UNSUPPORTED,
-                "with several K-segments K must be <= %d (int32 running sums over all of K); K=%lld",
-                SEGQ_MAX_KSEG_WIDTH, (long long)K);
-  if (M == 0) return ok();
-  sq::GemmProblem p{};
-  p.M = M; p.N = N; p.K = K;
-  p.x = x_bf16; p.ld_x = ld_x;
-  p.xq = xq; p.ld_q = ld_q; p.q_layout = q_layout;
-  p.w_packed = w_packed; p.w_scale = w_scale; p.act = act_scales;
-  p.ks = ks;
-  p.y = y_bf16; p.ld_y = ld_y; p.acc_debug = acc_debug;
-  p.single_scale = (flags & SEGQ_GEMM_SINGLE_SCALE) != 0;
-  const int kernel = segquant_gemm_kernel_for(M, N, K, flags);
-  // 4-bit weights: the streaming small-M kernel reads them as they are;
-  // every other path first widens them to int8 tiles in the workspace
-  const size_t widen = w4_widen_bytes(kernel, M, N, K, ks, flags, x_bf16 != nullptr);
-  if (widen && (!workspace || workspace_bytes < widen))
-    return fail(SEGQ_ERR_UNSUPPORTED,
-                "4-bit weights on this shape need a workspace of at least %zu bytes "
-                "(segquant_gemm_workspace_bytes)", widen);
-  p.w4 = (flags & SEGQ_GEMM_W4) && !widen;
-  if (widen) {
-    int8_t *w8 = static_cast<int8_t *>(workspace);
-    hipError_t e = sq::launch_widen_w4(w_packed, K, N, w8, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e, "widen launch");
-    p.w_packed = w8;
-  }
-  uint8_t *ws_rest = workspace ? static_cast<uint8_t *>(workspace) + widen : nullptr;
-  const size_t ws_rest_bytes = workspace ? workspace_bytes - widen : 0;
-  if (x_bf16 && ws_rest && quantize_first(kernel, M, N, ks, flags) &&
-      ws_rest_bytes >= (size_t)(M * K)) {
-    // quantise once into the workspace, then the GEMM from the signed codes
-    int8_t *codes = reinterpret_cast<int8_t *>(ws_rest);
-    hipError_t e = sq::launch_quantize(x_bf16, M, K, ld_x, ks, act_scales, codes, K,
-                                       SEGQ_Q_SIGNED, p.single_scale, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e, "quantize launch");
-    p.x = nullptr;
-    p.ld_x = 0;
-    p.xq = codes;
-    p.ld_q = K;
-    p.q_layout = SEGQ_Q_SIGNED;
-  }
-  hipError_t e = kernel == SEGQ_KERNEL_SMALLM ? sq::launch_gemm_smallm(p, (hipStream_t)stream)
-                                              : sq::launch_gemm_tile(p, (hipStream_t)stream);
-  return hip_status(e, "gemm launch");
+  int st = sq::gemm_validate(c, ks);
+  if (st) return st;
+  return sq::gemm_enqueue(c, ks, workspace, workspace ? workspace_bytes : 0);
 }
 
 }  // extern "C"

@@ -105,14 +105,16 @@ def segs(widths):
 
 def gemm(M=64, N=64, K=128, x=FAKE, ld_x=None, xq=None, ld_q=0, q_layout=0, w=FAKE, ws=FAKE,
          widths=None, off=None, act=FAKE, y=FAKE, ld_y=None, acc=None, flags=0, n_kseg=None,
-         work=None, work_bytes=0):
+         work=None, work_bytes=0, noalloc=False):
     o, wd = segs(widths if widths is not None else [K])
     if off is not None:
         o = np.asarray(off, np.int32)
-    return lib().segquant_gemm_w8a8_seg(
-        M, N, K, x, K if ld_x is None else ld_x, xq, ld_q, q_layout, w, ws,
-        len(wd) if n_kseg is None else n_kseg, o.ctypes.data_as(P), wd.ctypes.data_as(P), act,
-        y, N if ld_y is None else ld_y, acc, work, work_bytes, flags, None)
+    args = (M, N, K, x, K if ld_x is None else ld_x, xq, ld_q, q_layout, w, ws,
+            len(wd) if n_kseg is None else n_kseg, o.ctypes.data_as(P), wd.ctypes.data_as(P), act,
+            y, N if ld_y is None else ld_y, acc)
+    if noalloc:  # the no-allocation entry point: same arguments less the workspace
+        return lib().segquant_gemm_w8a8_seg_noalloc(*args, flags, None)
+    return lib().segquant_gemm_w8a8_seg(*args, work, work_bytes, flags, None)
 
 
 @pytest.mark.parametrize("kwargs,status", [
@@ -151,9 +153,21 @@ def gemm(M=64, N=64, K=128, x=FAKE, ld_x=None, xq=None, ld_q=0, q_layout=0, w=FA
     (dict(flags=32), S.SEGQ_ERR_SHAPE),
     (dict(x=None, xq=FAKE, ld_q=128, q_layout=1, flags=8), S.SEGQ_ERR_UNSUPPORTED),
 ])
-def test_gemm_validation(kwargs, status):
-    assert gemm(**kwargs) == status
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_gemm_validation(kwargs, status, noalloc):
+    assert gemm(noalloc=noalloc, **kwargs) == status
     assert S.segquant_last_error() != ""
+
+
+def test_noalloc_refuses_a_widening_beyond_its_scratch():
+    """4-bit weights off the streaming kernel are widened to K*N int8 bytes;
+    beyond the no-allocation call's scratch that is refused before any HIP
+    call (a quantise-first workspace beyond it is not needed: the call then
+    quantises inside the GEMM)."""
+    K, N = 8192, 16384  # 128 MiB widened
+    assert K * N > S.SEGQ_NOALLOC_SCRATCH_BYTES
+    assert gemm(M=64, N=N, K=K, flags=S.SEGQ_GEMM_W4, noalloc=True) == S.SEGQ_ERR_UNSUPPORTED
+    assert "scratch" in S.segquant_last_error()
 
 
 def test_gemm_w4_needs_a_workspace_off_the_streaming_kernel():
