@@ -291,9 +291,8 @@ int segquant_unpack_weight(const int8_t *w_packed, int64_t K, int64_t N, int8_t 
  *              the quantise-first bytes; segquant_gemm_workspace_bytes with
  *              the same flags gives the total), else SEGQ_ERR_UNSUPPORTED.
  * Requires K % 64 == 0, N % 16 == 0, every K-segment width <=
- * SEGQ_MAX_KSEG_WIDTH (and, with more than one K-segment, K itself <=
- * SEGQ_MAX_KSEG_WIDTH: SEGQ_ERR_UNSUPPORTED otherwise, as the large-M kernel
- * keeps int32 running sums over all of K), 16-byte aligned tensor pointers, ld_x and ld_q
+ * SEGQ_MAX_KSEG_WIDTH (each segment's int32 sums stay below 2^31; K itself
+ * has no further bound), 16-byte aligned tensor pointers, ld_x and ld_q
  * multiples of 8 and 16 elements, ld_y a multiple of 2.  M may be 0 (no
  * launch).  SEGQ_GEMM_FORCE_SMALLM requires M <= 16.
  */

@@ -19,8 +19,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OUT = os.path.join(HERE, "libsegquant.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "act_kernels.hip", "weight_kernels.hip", "gemm_tile.hip", "gemm_smallm.hip",
-           "noalloc.hip"]
+SOURCES = ["api.cpp", "act_kernels.hip", "weight_kernels.hip", "gemm_tile.hip", "gemm_lds.hip",
+           "gemm_smallm.hip", "noalloc.hip"]
 # ceiling probes for the benchmark (matrix-core-only loop, streaming read):
 # a library of their own, not part of the layer's
 PROBE_SOURCES = ["probes.hip"]

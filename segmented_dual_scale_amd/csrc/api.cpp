@@ -157,10 +157,6 @@ int gemm_validate(const GemmCall &c, SegTable &ks) {
   }
   if ((st = read_kseg(c.n_kseg, c.kseg_offset, c.kseg_width, c.K, SEGQ_MAX_KSEG_WIDTH, ks)))
     return st;
-  if (ks.n > 1 && c.K > SEGQ_MAX_KSEG_WIDTH)
-    return fail(SEGQ_ERR_UNSUPPORTED,
-                "with several K-segments K must be <= %d (int32 running sums over all of K); K=%lld",
-                SEGQ_MAX_KSEG_WIDTH, (long long)c.K);
   return ok();
 }
 

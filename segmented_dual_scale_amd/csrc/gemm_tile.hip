@@ -47,8 +47,10 @@
 //       STEP    every K-segment is one 64-wide k-step (one attention head per
 //               segment): each k-step's products start from zero and are
 //               folded into an fp32 sum held in registers.
-//       MULTI   general segments (MULTI64 when a segment ends inside a
-//               128-wide stage).  The int32 sums S run over all of K and are
+//       MULTI   general segments on bf16 input with K up to 132104
+//               (MULTI64 when a segment ends inside a 128-wide stage; other
+//               multi-segment calls go to the LDS-staged kernel of
+//               gemm_lds.hip).  The int32 sums S run over all of K and are
 //               never reset; at the end of segment i the fold adds
 //               (c_i - c_{i+1}) * S_i (c_i = s_i * s_w,i per column and half,
 //               c past the last segment = 0), which telescopes to
@@ -76,6 +78,8 @@ namespace {
 constexpr int kAPitch = 144;  // bytes per LDS row of one A plane (128 + 16 pad)
 constexpr int kBK = 128;      // K per LDS stage
 constexpr int kSmallTileGrid = 128;  // single segment: below this many 64 x 384 tiles, use 32 x 128
+// MULTI keeps int32 sums over all of K: |sum| <= K * 128 * 127 < 2^31
+constexpr int64_t kRunningSumMaxK = 132104;
 
 // Activation input: bf16 (quantised here), signed codes, two planes; and the
 // single-scale forms of the first two (one product on the signed code, the
@@ -750,6 +754,10 @@ hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s) {
     return launch_variant<64, 384, SINGLE>(t, amode, debug, s);
   }
   if (every_step) return launch_variant<32, 256, STEP>(t, amode, debug, s);
+  // Several K-segments on int8 codes, or a K beyond what MULTI's running
+  // int32 sums hold (K * 128 * 127 < 2^31): the kernel that stages both
+  // operands through LDS and folds each segment's own sums.
+  if (!p.x || p.K > kRunningSumMaxK) return launch_gemm_lds(p, s);
   bool even_ends = true;  // every segment end but the last on a whole stage
   for (int i = 0; i + 1 < p.ks.n; ++i) even_ends = even_ends && (p.ks.end[i] % 128 == 0);
   hipError_t e = even_ends ? launch_variant<64, 256, MULTI>(t, amode, debug, s)

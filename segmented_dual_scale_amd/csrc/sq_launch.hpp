@@ -69,6 +69,8 @@ struct GemmProblem {
 
 hipError_t launch_gemm_tile(const GemmProblem &p, hipStream_t s);
 hipError_t launch_gemm_smallm(const GemmProblem &p, hipStream_t s);
+// the large-M kernel with both operands staged through LDS
+hipError_t launch_gemm_lds(const GemmProblem &p, hipStream_t s);
 
 constexpr int kSmallMMax = 16;
 

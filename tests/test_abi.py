@@ -147,7 +147,6 @@ def gemm(M=64, N=64, K=128, x=FAKE, ld_x=None, xq=None, ld_q=0, q_layout=0, w=FA
     (dict(widths=[128], n_kseg=0), S.SEGQ_ERR_SEGMENTS),
     (dict(K=64 * 129, widths=[64] * 129), S.SEGQ_ERR_UNSUPPORTED),
     (dict(K=132160, widths=[132160]), S.SEGQ_ERR_UNSUPPORTED),  # int32 bound
-    (dict(K=132160, widths=[66048, 66112]), S.SEGQ_ERR_UNSUPPORTED),  # running sums over all of K
     (dict(M=17, flags=S.SEGQ_GEMM_FORCE_SMALLM), S.SEGQ_ERR_UNSUPPORTED),
     (dict(flags=3), S.SEGQ_ERR_SHAPE),
     (dict(flags=32), S.SEGQ_ERR_SHAPE),
@@ -180,6 +179,17 @@ def test_gemm_w4_needs_a_workspace_off_the_streaming_kernel():
     # the streaming small-M kernel reads the 4-bit tiles itself
     assert S.segquant_gemm_workspace_bytes(2, 9216, 1536, None, S.SEGQ_GEMM_W4) == 0
     assert S.segquant_weight_packed_bytes(1536, 9216) == 2 * S.load_library().segquant_weight_packed_bytes_w4(1536, 9216)
+
+
+def test_gemm_accepts_several_segments_beyond_the_int32_bound_of_k():
+    """Only each K-segment's width is bounded (its int32 sums); a K above that
+    bound split into narrower segments passes validation (and asks for no
+    workspace: the segments are folded inside the GEMM)."""
+    K = 132160
+    assert S.segquant_gemm_workspace_bytes(40, 64, K, [66048, 66112]) == 0
+    assert S.segquant_last_error() == ""
+    assert S.segquant_gemm_workspace_bytes(40, 64, K, [K]) == 0
+    assert "int32 bound" in S.segquant_last_error()
 
 
 def test_gemm_misaligned_workspace():

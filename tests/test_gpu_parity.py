@@ -325,6 +325,64 @@ def test_gemm_at_the_int32_bound(M, mode, nk):
     assert ok, f"Y out of tolerance: {nbad} elements, worst excess {worst}"
 
 
+@pytest.mark.parametrize("M", [2, 40])
+@pytest.mark.parametrize("mode", ["bf16", "signed", "planes", "single"])
+def test_gemm_k_beyond_the_int32_bound_in_segments(M, mode):
+    """K = 264192, twice SEGQ_MAX_KSEG_WIDTH's multiple of 64, as two
+    K-segments of 132096, each driven to its own int32 limit (the operands of
+    test_gemm_at_the_int32_bound): only each segment's sums must fit in int32
+    ([P1] "SegLinear", input-segmented sum of per-segment products), so every
+    per-segment accumulator is exact although their total is not an int32.
+    Streaming small-M kernel (M = 2) and the large-M kernel that folds each
+    segment's own sums (M = 40), every input mode and the single-scale
+    product; accumulators bit-exact, Y within tolerance."""
+    K1, N = 132096, 32
+    kseg = [K1, K1]
+    K = 2 * K1
+    x = np.ones((M, K), np.float32)
+    x[0::2] = -1.0
+    g = np.random.default_rng(11)
+    if M > 4:
+        x[4:8] = g.uniform(-1.0, 1.0, (4, K)).astype(np.float32)
+    w = np.full((K, N), 0.02, np.float32)
+    w[:, 0::2] = -0.02
+    w[:, 8:12] = (g.standard_normal((K, 4)) * 0.02).astype(np.float32)
+    xb = W.f32_to_bf16_bits(x)
+    gpu = GpuLayer(xb, w, kseg, None, True)
+    if mode == "single":
+        import torch
+        s1, s2, inv, inv2 = oracle.calibrate_amax_single(xb, kseg)
+        wq, ws = oracle.quantize_weight(w, kseg, None, True)
+        qp, qn = oracle.quantize_dualscale(xb, kseg, inv, inv2)
+        acc_ref = oracle.segment_acc(qp, qn, wq, kseg)
+        y_ref = oracle.dequantize(acc_ref, s1, s2, ws)
+        act = S.segquant_calibrate_amax_single(gpu.xd, kseg)
+        xq = S.segquant_quantize_dualscale(gpu.xd, act, kseg, S.SEGQ_Q_SIGNED)
+        for src in ("bf16", "signed"):
+            acc = torch.full((2, len(kseg), M, N), -7, dtype=torch.int32, device=DEV)
+            if src == "bf16":
+                y = S.segquant_gemm_w8a8_seg(gpu.xd, gpu.wp, gpu.ws, act, kseg, acc_debug=acc,
+                                             flags=S.SEGQ_GEMM_SINGLE_SCALE)
+            else:
+                y = S.segquant_gemm_w8a8_seg(None, gpu.wp, gpu.ws, act, kseg, xq=xq, N=N,
+                                             acc_debug=acc, flags=S.SEGQ_GEMM_SINGLE_SCALE)
+            a = acc.cpu().numpy()
+            assert np.array_equal(a[0], acc_ref[0] + acc_ref[1]), f"single-scale products ({src})"
+            assert np.all(a[1] == -7), f"plane 1 was written ({src})"
+            ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), y_ref)
+            assert ok, f"single-scale Y ({src}): {nbad} elements, worst excess {worst}"
+        return
+    ref = OracleLayer(xb, w, kseg, None, True)
+    assert int(np.abs(ref.acc.astype(np.int64)).max()) == K1 * 128 * 127
+    assert int(np.abs(ref.acc.astype(np.int64).sum(axis=1)).max()) > 2**31 - 1
+    y, acc = gpu.run(mode, debug=True)
+    assert np.array_equal(acc.cpu().numpy(), ref.acc)
+    ok, worst, nbad = y_tolerance_ok(bf16_dev_to_f64(y), ref.y)
+    assert ok, f"Y out of tolerance: {nbad} elements, worst excess {worst}"
+    y2, _ = gpu.run(mode, debug=False)
+    assert np.array_equal(bf16_dev_to_f64(y2), bf16_dev_to_f64(y))
+
+
 @pytest.mark.parametrize("M", [3, 40])
 @pytest.mark.parametrize("mode", ["bf16", "signed", "planes"])
 @pytest.mark.parametrize("case", ["x_zero", "w_zero", "one_segment_zero", "one_group_zero"])
