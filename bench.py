@@ -56,7 +56,9 @@ CSRC = os.path.join(ROOT, "segmented_dual_scale_amd", "csrc")
 KERNEL_SOURCES = {
     "gemm_smallm_kernel": ["gemm_smallm.hip", "sq_device.hpp", "sq_launch.hpp"],
     "gemm_tile_kernel": ["gemm_tile.hip", "sq_device.hpp", "sq_launch.hpp"],
+    "gemm_lds_kernel": ["gemm_lds.hip", "sq_device.hpp", "sq_launch.hpp"],
 }
+RUNNING_SUM_MAX_K = 132104  # K * 128 * 127 < 2^31: the tile kernel's running int32 sums
 # The pages' own timing figures: whole-model, per denoising step, not per layer.
 PAGES_LATENCY = ("hliangzhao.me 'SegQuant' page, deployment-cost table (SD3.5 on an RTX 4090, "
                  "whole backbone per sampling step): FP16 317.18 ms, INT8 baseline 278.86 ms, "
@@ -75,6 +77,32 @@ def alg_ops(wl) -> int:
 def hbm_bound(wl) -> bool:
     # ridge of MI355X: 5.0e15 ops / 8.0e12 B/s = 625 ops per byte
     return alg_ops(wl) / alg_bytes(wl) < 625.0
+
+
+def gemm_kernel_name(M: int, K: int, kseg, codes: bool, smallm: bool) -> str:
+    """The kernel that runs the GEMM launch of a call: the streaming small-M
+    kernel; the LDS-staged kernel for several K-segments on int8 codes (or K
+    beyond the running-sum bound); otherwise the tile kernel (one segment, or
+    every segment one 64-wide step)."""
+    if smallm:
+        return "gemm_smallm_kernel"
+    widths = list(kseg)
+    if len(widths) > 1 and any(w != 64 for w in widths) and (codes or K > RUNNING_SUM_MAX_K):
+        return "gemm_lds_kernel"
+    return "gemm_tile_kernel"
+
+
+def workload_kernel(S, wl, mode: str) -> str:
+    """gemm_kernel_name for a workload run in one of the bench's modes."""
+    flags = {"single": S.SEGQ_GEMM_SINGLE_SCALE, "w4": S.SEGQ_GEMM_W4}.get(mode, S.SEGQ_GEMM_AUTO)
+    kseg = list(wl.kseg)
+    smallm = S.segquant_gemm_kernel_for(wl.M, wl.N, wl.K, flags) == S.SEGQ_KERNEL_SMALLM
+    # the workspace holds the int8 widening of 4-bit weights (K*N, off the
+    # small-M path) and, when the call quantises first, the M*K codes
+    widen = wl.K * wl.N if mode == "w4" and not smallm else 0
+    codes = mode in ("signed", "planes") or \
+        S.segquant_gemm_workspace_bytes(wl.M, wl.N, wl.K, kseg, flags) - widen >= wl.M * wl.K
+    return gemm_kernel_name(wl.M, wl.K, kseg, codes, smallm)
 
 
 def source_digest(kernel: str) -> str:
@@ -286,8 +314,7 @@ class Layer:
         self.wps = [wp] + [wp.clone() for _ in range(R - 1)]
         self.ys = [torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
         torch.cuda.synchronize()
-        kid = S.segquant_gemm_kernel_for(wl.M, wl.N, wl.K)
-        self.kernel = "gemm_smallm_kernel" if kid == S.SEGQ_KERNEL_SMALLM else "gemm_tile_kernel"
+        self.kernel = workload_kernel(S, wl, mode)
         # the library's choice of quantising first (one workspace, reused by
         # every call, as a layer would)
         nb = S.segquant_gemm_workspace_bytes(wl.M, wl.N, wl.K, self.kseg, self.flags) \
@@ -714,16 +741,18 @@ def main():
         summarize_pmc(args.summarize_pmc)
         return
     if args.ingest_trace:
+        import segmented_dual_scale_amd as S
         import segmented_dual_scale_amd.workloads as W
         wl = W.WORKLOADS[args.workload]
-        kernel = "gemm_smallm_kernel" if wl.M <= 16 else "gemm_tile_kernel"
+        kernel = workload_kernel(S, wl, args.mode)
         cmd = args.trace_command or "(command not given)"
         ingest_trace(args.ingest_trace, args.workload, args.mode, kernel, cmd, args.steps)
         return
     if args.ingest_pmc:
+        import segmented_dual_scale_amd as S
         import segmented_dual_scale_amd.workloads as W
         wl = W.WORKLOADS[args.workload]
-        kernel = "gemm_smallm_kernel" if wl.M <= 16 else "gemm_tile_kernel"
+        kernel = workload_kernel(S, wl, args.mode)
         cmd = f"python3 bench.py --workload {args.workload} --mode {args.mode} --pmc-pass"
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload, args.mode, kernel, cmd)
         return

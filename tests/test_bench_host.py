@@ -132,3 +132,33 @@ def test_trace_record_written_and_read_back(tmp_path, monkeypatch, capsys):
     path = tmp_path / "profiles" / f"trace_{kernel}_{wl}.txt"
     path.write_text(path.read_text().replace(B.source_digest(kernel), "0" * 64))
     assert B.read_trace(kernel, wl, "bf16") is None
+
+
+def test_kernel_named_for_each_workload_and_mode():
+    """The roofline and profile records name the kernel that runs the GEMM
+    launch: the LDS-staged kernel for c5 (four K-segments of 3072, codes
+    from the quantise-first launch or the caller), the tile kernel for one
+    segment or 64-wide head segments, the streaming kernel at small M."""
+    B = _bench()
+    import segmented_dual_scale_amd as S
+    from segmented_dual_scale_amd import workloads as W
+    expect = {
+        ("c1_tiny_outseg", "bf16"): "gemm_tile_kernel",
+        ("c2_adanorm_gemv", "bf16"): "gemm_smallm_kernel",
+        ("c2_adanorm_gemv", "w4"): "gemm_smallm_kernel",
+        ("c3_dit_ffn_fc2", "bf16"): "gemm_tile_kernel",
+        ("c3_dit_ffn_fc2", "signed"): "gemm_tile_kernel",
+        ("c3_dit_ffn_fc2", "w4"): "gemm_tile_kernel",
+        ("c4_attn_out_inseg", "bf16"): "gemm_tile_kernel",
+        ("c5_flux_ffn_fc2", "bf16"): "gemm_lds_kernel",
+        ("c5_flux_ffn_fc2", "signed"): "gemm_lds_kernel",
+        ("c5_flux_ffn_fc2", "planes"): "gemm_lds_kernel",
+        ("c5_flux_ffn_fc2", "single"): "gemm_lds_kernel",
+        ("c5_flux_ffn_fc2", "w4"): "gemm_lds_kernel",
+    }
+    for (name, mode), kernel in expect.items():
+        assert B.workload_kernel(S, W.WORKLOADS[name], mode) == kernel, (name, mode)
+    # fused bf16 input beyond the running-sum bound takes the LDS kernel too
+    assert B.gemm_kernel_name(64, 2 * 66112, [66112, 66112], False, False) == "gemm_lds_kernel"
+    assert B.gemm_kernel_name(64, 2 * 3072, [3072, 3072], False, False) == "gemm_tile_kernel"
+    assert B.gemm_kernel_name(64, 128, [64, 64], True, False) == "gemm_tile_kernel"
