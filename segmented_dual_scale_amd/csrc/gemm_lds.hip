@@ -35,11 +35,12 @@
 //         ahead (sign picks the half's inverse scale, one fp32 multiply,
 //         clamp, round half to even) and written as the + and - planes in the
 //         same rotated layout.
-//   * One barrier per stage, in its middle: after it the next stage's
-//     operands are read while the second half of this stage's products
-//     hides their latency, and this stage's buffer takes the copies of stage
-//     u + NST.  Before it, this wave waits for its own copies into stage
-//     u + 1 only; later stages' copies stay in flight.  The waits are
+//   * Each 32-k sub-step's operands are read from LDS one sub-step ahead of
+//     its products.  One barrier per stage, between its two sub-steps: after
+//     it the next stage's first operands are read while this stage's second
+//     sub-step hides their latency, and this stage's buffer takes the copies
+//     of stage u + NST.  Before it, this wave waits for its own copies into
+//     stage u + 1 only; later stages' copies stay in flight.  The waits are
 //     explicit: the compiler does not count the global->LDS copies.
 //   * Signed-code input: the codes feed one product directly (A_t = Q W) and
 //     their + plane, split off in registers, the other (A+ = P W).  The fold
@@ -361,23 +362,25 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(LdsArgs a) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) yacc[i][j] = v16f{};
 
-  // products of one 32-k sub-step for output blocks [B0, B1) (block index
-  // mb * NB + nb); ZERO: the products start from zero (a segment's first)
-  auto mma = [&](const Frags &f, bool zero, int B0, int B1) __attribute__((always_inline)) {
+  // products of one 32-k sub-step; ZERO: they start from zero (a segment's
+  // first).  The products on the codes as read (signed code, or the - plane)
+  // come first, so that they can run while the + plane is split off.
+  auto mma = [&](const Frags &f, bool zero) __attribute__((always_inline)) {
+    if (!ONE) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const v4u &qb = DERIVE ? f.a[mb][0] : f.a[mb][1];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[1][mb][nb] = mfma(qb, f.b[nb], zero ? v16i{} : acc[1][mb][nb]);
+      }
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      if ((mb + 1) * NB <= B0 || mb * NB >= B1) continue;
       const v4u &pa = DERIVE ? f.p[mb] : f.a[mb][0];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int blk = mb * NB + nb;
-        if (blk < B0 || blk >= B1) continue;
+      for (int nb = 0; nb < NB; ++nb)
         acc[0][mb][nb] = mfma(pa, f.b[nb], zero ? v16i{} : acc[0][mb][nb]);
-        if (!ONE) {
-          const v4u &qb = DERIVE ? f.a[mb][0] : f.a[mb][1];
-          acc[1][mb][nb] = mfma(qb, f.b[nb], zero ? v16i{} : acc[1][mb][nb]);
-        }
-      }
     }
   };
 
@@ -438,16 +441,18 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(LdsArgs a) {
   // ---- the pipeline ----
   // Stage u (64 k) is read from buffer u % NST.  Its copies were issued
   // NST stages earlier, right after the barrier that freed that buffer.
-  // Within stage u: the sub-step-1 operands are read, (bf16) stage u+1 is
-  // quantised into its buffer, the sub-step-0 products and the first half
-  // of the sub-step-1 products are issued; then this wave waits for its
-  // copies into stage u+1, and the barrier makes every wave's copies and
-  // quantised codes of stage u+1 visible and proves buffer u no longer read;
-  // the copies of stage u+NST go into buffer u, the sub-step-0 operands of
-  // stage u+1 are read, and the second half of the products follows, hiding
-  // the reads' latency.  Per stage and wave, in order: (bf16) the loads of
-  // stage u+3 into the slot stage u+1 used, then the stage's copies.
-  constexpr int NBLK = MB * NB, HALF = (NBLK + 1) / 2;
+  // Each 32-k sub-step's operands are read from LDS one sub-step ahead of
+  // their products.  Within stage u: the sub-step-1 operands are read;
+  // sub-step 0's products run (operands read during stage u - 1), with
+  // (bf16) the quantisation of stage u + 1 between them; this wave waits
+  // for its copies into stage u + 1 and for its reads of buffer u, and the
+  // barrier makes every wave's copies and quantised codes of stage u + 1
+  // visible and proves buffer u no longer read; the copies of stage u + NST
+  // go into buffer u, stage u + 1's sub-step-0 operands are read, and
+  // sub-step 1's products hide those reads.  Per stage and wave, in order:
+  // (bf16) the loads of stage u + 3 into the slot stage u + 1 used, then the
+  // stage's copies.
+  constexpr int NBLK = MB * NB;
   auto issue = [&](auto XSLOT, int s, int buf) __attribute__((always_inline)) {
     if (BF16) load_x(XSLOT, s - NST + 3);
     copy_stage(s, buf);
@@ -472,7 +477,8 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(LdsArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   Frags f0, f1;
   read_frags(f0, smem, 0);
-  derive(f0);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
 
   float wsf[NB];  // the weight scales of the segment being folded
   int buf = 0;
@@ -487,49 +493,37 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(LdsArgs a) {
     }
   };
   constexpr int NM_SUB = NACC * NBLK;                        // products of one sub-step
-  constexpr int NM_H1 = NACC * HALF, NM_H2 = NM_SUB - NM_H1;  // the two halves of sub-step 1
   constexpr int V_DER = DERIVE ? MB * 4 * 3 : 0;              // + plane split of one sub-step
   constexpr int V_Q = BF16 ? XP * (ONE ? 44 : 52) : 0;        // quantisation of one stage
   auto stage = [&](auto XSLOT, int u, bool first, bool last_of_seg) __attribute__((always_inline)) {
     constexpr int xs = decltype(XSLOT)::value;  // bf16: the slot of stage u + 1 ((u + 1) % 2)
     const uint8_t *sb = smem + buf * ST;
     const int nbuf = buf == NST - 1 ? 0 : buf + 1;
-    // (1) sub-step 1's operands, read now so their latency hides behind
-    //     sub-step 0's products (nothing is pending here: the explicit wait
-    //     keeps the compiler from waiting for these reads before them)
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_sched_barrier(0);
+    // (1) sub-step 1's operands: their latency hides behind sub-step 0
     read_frags(f1, sb, 1);
     __builtin_amdgcn_sched_barrier(0);
-    // (2) sub-step 0's products (their + plane was split off at the end of
-    //     the previous stage), with (bf16) the quantisation of stage u + 1
-    //     and the split of sub-step 1's + plane between them
+    // (2) sub-step 0: the + plane split off (before the products in program
+    //     order, which read it; the products on the codes as read can run
+    //     meanwhile) and (bf16) the quantisation of stage u + 1, spread
+    //     between the products
+    derive(f0);
     if (first) {
-      mma(f0, true, 0, NBLK);
+      mma(f0, true);
     } else {
-      mma(f0, false, 0, NBLK);
+      mma(f0, false);
     }
     if (BF16) quant_stage(lc<xs>{}, u + 1, nbuf);
-    derive(f1);
-    {
-      // (codes: a few products first, while sub-step 1's reads land)
-      constexpr int LEAD = BF16 ? 0 : 3;
-      if (LEAD > 0) __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
-      constexpr int REST = NM_SUB - LEAD;
-      interleave(lc<REST>{}, lc<(V_Q + V_DER + REST - 1) / REST>{});
-    }
+    interleave(lc<NM_SUB>{}, lc<(V_Q + V_DER + NM_SUB - 1) / NM_SUB>{});
     __builtin_amdgcn_sched_barrier(0);
-    // (3) the first half of sub-step 1's products
-    mma(f1, false, 0, HALF);
     if (last_of_seg) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         wsf[nb] = *reinterpret_cast<const float *>(sb + WS_OFF + 4 * (wn * WN + 32 * nb + (lane & 31)));
     }
     __builtin_amdgcn_sched_barrier(0);
-    // (4) this wave's copies into stage u + 1 have landed; after the barrier
-    //     every wave's have, every wave's quantised codes of stage u + 1 are
-    //     written, and buffer u is no longer read
+    // (3) this wave's copies into stage u + 1 have landed and its reads of
+    //     buffer u are done; after the barrier every wave's are, and every
+    //     wave's quantised codes of stage u + 1 are written
     if (DEBUG) {
       wait_vm<0, true>();  // (the accumulator dump's stores also count)
     } else {
@@ -538,24 +532,18 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(LdsArgs a) {
     }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // (5) the copies of stage u + NST into buffer u (bf16: the loads of
+    // (4) the copies of stage u + NST into buffer u (bf16: the loads of
     //     stage u + 3 into the slot just quantised), and stage u + 1's
     //     sub-step-0 operands
     issue(lc<xs>{}, u + NST, buf);
     read_frags(f0, smem + nbuf * ST, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // (6) the second half of sub-step 1's products hides those reads; the
-    //     + plane of stage u + 1's sub-step 0 is split off between the last
-    //     of them.  The stage ends with every LDS read complete, so the next
-    //     stage's first products wait for nothing.
-    mma(f1, false, HALF, NBLK);
-    derive(f0);
-    {
-      constexpr int LEAD = NM_H2 > 4 ? 4 : NM_H2 - 1;
-      __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
-      constexpr int REST = NM_H2 - LEAD;
-      interleave(lc<REST>{}, lc<(V_DER + REST - 1) / REST>{});
-    }
+    // (5) sub-step 1, as sub-step 0, hiding those reads; the stage ends with
+    //     every LDS read complete, so the next stage's products wait for
+    //     nothing
+    derive(f1);
+    mma(f1, false);
+    interleave(lc<NM_SUB>{}, lc<(V_DER + NM_SUB - 1) / NM_SUB>{});
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_sched_barrier(0);
