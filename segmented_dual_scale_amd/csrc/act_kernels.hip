@@ -352,6 +352,13 @@ void plan_rows(int64_t M, const SegTable &ks, ActArgs &a, int64_t elems = 16384)
   int64_t rows_per_step = (64 >> lg) * 4;
   int64_t rows = (elems + wmax - 1) / wmax;
   rows = ((rows + rows_per_step - 1) / rows_per_step) * rows_per_step;
+  // at most about four 16-byte pieces per thread: one batch of loads in
+  // flight each, and more workgroups for narrow segments (24 segments of
+  // 64: 7.5 instead of 8.3 us on MI355X)
+  const int64_t per_row = (chunks + (1 << lg) - 1) >> lg;  // pieces per thread per row
+  int64_t r4 = (4 * rows_per_step + per_row - 1) / per_row;
+  r4 = ((r4 + rows_per_step - 1) / rows_per_step) * rows_per_step;
+  if (r4 < rows) rows = r4;
   if (rows > M) rows = M < 1 ? 1 : M;
   a.rows_per_block = (int32_t)rows;
 }
