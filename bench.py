@@ -431,7 +431,7 @@ class Layer:
         self.xs = self.xqs = self.wps = self.ys = self.work = None
 
 
-def measured_peaks(dev, stream, slab_bytes: int = 0):
+def measured_peaks(dev, stream, slab_bytes: int = 0, sustain_s: float = 1.0):
     """Ceilings measured on this GPU by the probe library: an int8
     matrix-core-only loop (one wave per SIMD and two), the shader clock while
     it runs, a streaming read and a device copy of 1 GiB, and (slab_bytes > 0)
@@ -489,6 +489,38 @@ def measured_peaks(dev, stream, slab_bytes: int = 0):
             clock = ratio * khz * 1e3 if khz > 0 else None
     out["int8_mfma_tops"] = best_tops
     out["shader_clock_ghz_under_mfma"] = clock / 1e9 if clock else None
+    # the same loop sustained: back-to-back launches for about `sustain_s`
+    # seconds, rate and clock over the last ones (the clock falls under a
+    # long matrix-core load; the layer kernels run that long in a serving loop)
+    if sustain_s > 0:
+        blocks = cus
+        waves = blocks * 4
+        sink = torch.empty(waves * 64, dtype=torch.int32, device=dev)
+        spans = torch.zeros(waves * 2, dtype=torch.int64, device=dev)
+
+        def run1():
+            rc = lib.sqprobe_mfma_i8(iters, blocks, 4, ctypes.c_void_p(sink.data_ptr()),
+                                     ctypes.c_void_p(spans.data_ptr()), sp)
+            if rc != 0:
+                raise RuntimeError(f"sqprobe_mfma_i8 failed ({rc})")
+        with torch.cuda.stream(stream):
+            t1 = timed(run1, 1)
+            n = max(32, int(sustain_s / t1))
+            last = 16
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for i in range(n):
+                if i == n - last:
+                    e0.record(stream)
+                run1()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / last
+        ops = waves * iters * lib.sqprobe_mfma_chains() * lib.sqprobe_ops_per_mfma()
+        sv = spans.view(-1, 2).cpu().double()
+        ratio = float((sv[:, 0] / sv[:, 1].clamp(min=1)).median())
+        out["mfma_loop_sustained_tops"] = ops / t / 1e12
+        out["shader_clock_ghz_sustained_mfma"] = ratio * khz * 1e3 / 1e9 if khz > 0 else None
+        out["mfma_loop_sustained_seconds"] = n * t
     nbytes = 1 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.fill_(1)
@@ -540,7 +572,9 @@ def measured_peaks(dev, stream, slab_bytes: int = 0):
     out["method"] = (f"probe library: int8 32x32x32 matrix-core loop, {lib.sqprobe_mfma_chains()} "
                      f"independent accumulators per wave, 4 waves per workgroup, 1 and 2 "
                      f"workgroups per CU ({cus} CUs), clock = shader/constant clock ratio "
-                     f"over the loop; grid-stride 16-byte read of 1 GiB; torch copy of 512 MiB; "
+                     f"over the loop; the 1-per-CU loop again back to back for about "
+                     f"{sustain_s:g} s, rate and clock over the last launches (sustained); "
+                     f"grid-stride 16-byte read of 1 GiB; torch copy of 512 MiB; "
                      f"best of 3-5 timed launches; slab: grid-stride reads of slab_bytes from "
                      f"{nbytes // max(slab_bytes, 1) if slab_bytes else 0} distinct slices, one launch "
                      f"each, replayed as a graph, best of {cus // 2}-{16 * cus} workgroups")
@@ -699,6 +733,47 @@ def summarize_pmc(run_dirs, match: str = "gemm_"):
             print(f"  {c:32s} {sum(v.values()) / len(v):14.6g}   ({len(v)} dispatches)")
 
 
+def summarize_clock(run_dir: str, match: str = "gemm_", xcds: int = 8):
+    """Shader clock during each layer kernel, from one rocprofv3 run that takes
+    GRBM_GUI_ACTIVE with --pmc and the dispatch times with --kernel-trace: the
+    counter (summed over the XCDs) divided by the XCD count is the kernel's
+    busy cycles, and those over its traced duration are the clock."""
+    cyc = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if match in r["Kernel_Name"] and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    key = (r["Kernel_Name"], r["Dispatch_Id"])
+                    cyc[key] = cyc.get(key, 0.0) + float(r["Counter_Value"])
+    dur = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if match in r["Kernel_Name"]:
+                    dur[(r["Kernel_Name"], r["Dispatch_Id"])] = \
+                        int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    per = {}
+    for key, c in cyc.items():
+        if key in dur and dur[key] > 0:
+            per.setdefault(key[0], []).append((c / xcds / dur[key], dur[key]))
+    if not per:
+        raise SystemExit(f"no dispatch under {run_dir} has both GRBM_GUI_ACTIVE and a trace span")
+    out = {}
+    for name in sorted(per):
+        ghz = sorted(g for g, _ in per[name])
+        us = sum(d for _, d in per[name]) / len(per[name]) / 1e3
+        out[name] = (_median(ghz), ghz[0], ghz[-1], len(ghz), us)
+        print(f"{name[:110]}\n  shader clock median {out[name][0]:.3f} GHz (min {ghz[0]:.3f}, "
+              f"max {ghz[-1]:.3f}) over {len(ghz)} dispatches, mean duration {us:.2f} us")
+    return out
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -726,6 +801,9 @@ def main():
                          "per layer kernel")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the counter record of --workload from two --pmc-pass runs")
+    ap.add_argument("--summarize-clock", metavar="DIR",
+                    help="shader clock per layer kernel from a rocprofv3 run with --pmc "
+                         "GRBM_GUI_ACTIVE and --kernel-trace")
     ap.add_argument("--ingest-trace", metavar="DIR",
                     help="write the kernel-trace record of --workload from a rocprofv3 "
                          "--kernel-trace run of the headline phase (--no-all --no-producer "
@@ -739,6 +817,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
+        return
+    if args.summarize_clock:
+        summarize_clock(args.summarize_clock)
         return
     if args.ingest_trace:
         import segmented_dual_scale_amd as S
@@ -885,9 +966,16 @@ def main():
             # a launch that only streams this call's weight, back to back
             roof["stream_floor_us"] = mp["hbm_stream_slab_us"]
             roof["over_stream_floor"] = roof["per_launch"]["avg_us"] / mp["hbm_stream_slab_us"]
+        sus = mp.get("mfma_loop_sustained_tops")
+        if roof["bound"] != "hbm" and sus:
+            roof["frac_of_sustained_mfma"] = roof["achieved"] / sus
         for v in line.get("all_workloads", {}).values():
             ref = mp["hbm_read_gbs"] if v["bound"] == "hbm" else mp["int8_mfma_tops"]
             v["frac_of_measured"] = v["value"] / ref
+            if v["bound"] != "hbm" and sus:
+                v["frac_of_sustained_mfma"] = v["value"] / sus
+                if v.get("gemm_us_per_launch"):
+                    v["gemm_frac_of_sustained_mfma"] = v["gemm_frac"] * PEAK_INT8_TOPS / sus
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, x_host, w_host)
     print(json.dumps(line), flush=True)

@@ -162,3 +162,29 @@ def test_kernel_named_for_each_workload_and_mode():
     assert B.gemm_kernel_name(64, 2 * 66112, [66112, 66112], False, False) == "gemm_lds_kernel"
     assert B.gemm_kernel_name(64, 2 * 3072, [3072, 3072], False, False) == "gemm_tile_kernel"
     assert B.gemm_kernel_name(64, 128, [64, 64], True, False) == "gemm_tile_kernel"
+
+
+def test_shader_clock_from_busy_cycles_over_trace_span(tmp_path, capsys):
+    """GRBM_GUI_ACTIVE is summed over the 8 XCDs: per XCD it is the kernel's
+    cycles, and those over the traced nanoseconds are GHz."""
+    B = _bench()
+    with open(tmp_path / "run_counter_collection.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writerow([1, "gemm_k", "GRBM_GUI_ACTIVE", 8 * 2300])      # 2300 cycles in 1000 ns
+        w.writerow([2, "gemm_k", "GRBM_GUI_ACTIVE", 8 * 2100 * 2])  # 4200 cycles in 2000 ns
+        w.writerow([3, "gemm_k", "GRBM_GUI_ACTIVE", 8 * 2200])      # 2200 cycles in 1000 ns
+        w.writerow([4, "other", "GRBM_GUI_ACTIVE", 5])
+    with open(tmp_path / "run_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writerow([1, "gemm_k", 0, 1000])
+        w.writerow([2, "gemm_k", 5000, 7000])
+        w.writerow([3, "gemm_k", 9000, 10000])
+        w.writerow([4, "other", 0, 10])
+    out = B.summarize_clock(str(tmp_path))
+    capsys.readouterr()
+    med, lo, hi, n, us = out["gemm_k"]
+    assert n == 3 and med == pytest.approx(2.2) and lo == pytest.approx(2.1) and hi == pytest.approx(2.3)
+    assert us == pytest.approx(4.0 / 3)
+    assert "other" not in out
