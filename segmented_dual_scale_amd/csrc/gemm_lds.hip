@@ -48,11 +48,14 @@
 //     A- = A_t - A+.  Two-plane and bf16 input multiply the planes as they
 //     are: y += c+ A+ + c- A-.  Single-scale: one product on the signed code.
 //     (c+-_i = s+-_i * w_scale[i][n].)
-//   * int8 input: 128 x 128 tiles, two workgroups per CU, 256 registers per
-//     lane each.  Measured on MI355X, the copies' load path is what bounds
-//     this kernel: the matrix cores run about twice as fast with the copies
-//     removed, and a wave that issues a copy behind misses still in flight
-//     stalls; a second workgroup's waves keep the matrix cores fed meanwhile.
+//   * int8 input: 64 x 64 per wave, two waves per SIMD (256 registers per
+//     lane each): signed codes on 128 x 256 tiles of eight waves, one
+//     workgroup per CU; two planes on 128 x 128 tiles of four, two per CU.
+//     Measured on MI355X, the copies' issue and the bytes moved bound this
+//     kernel more than the matrix cores: without the copies it runs about
+//     a fifth faster, and the shader clock under it falls well below the
+//     clock of a matrix-core-only loop.  The wider tile copies a quarter
+//     fewer bytes per product.
 //   * Tile order is XCD-aware: workgroups are dealt to the 8 XCDs in turn, so
 //     XCD x receives one contiguous range of logical tiles, ordered in
 //     groups of 8 row tiles so that the tiles one XCD runs at once share
@@ -135,9 +138,9 @@ __device__ __forceinline__ void lds_dma16(const void *g, uint8_t *l) {
   __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 16, 0, 0);
 }
 
-template <int BM, int BN, int WGM, int AM, int NST, bool DEBUG, int OCC>
-__global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(LdsArgs a) {
-  constexpr int WGN = 4 / WGM;
+template <int BM, int BN, int WGM, int AM, int NST, bool DEBUG, int OCC, int NWV>
+__global__ __launch_bounds__(64 * NWV, OCC) void gemm_lds_kernel(LdsArgs a) {
+  constexpr int WGN = NWV / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN, MB = WM / 32, NB = WN / 32;
   constexpr bool BF16 = AM == LA_BF16 || AM == LA_BF16_1;
   constexpr bool ONE = AM == LA_BF16_1 || AM == LA_SIGNED_1;
@@ -145,15 +148,18 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(LdsArgs a) {
   constexpr int NPL = (AM == LA_PLANES || AM == LA_BF16) ? 2 : 1;  // activation planes in LDS
   constexpr int A_PL = BM * 64;   // bytes of one activation plane per stage
   constexpr int W_ST = BN * 64;   // bytes of weight per stage
-  constexpr int NWS = (BN + 255) / 256;  // 4-byte copies per wave per stage of the weight scales
+  constexpr int NWS = (BN + 64 * NWV - 1) / (64 * NWV);  // 4-byte copies per wave per stage of the weight scales
   constexpr int WS_OFF = W_ST + NPL * A_PL;  // the stage's weight-scale row (fp32 per column)
-  constexpr int ST = WS_OFF + NWS * 1024;
-  constexpr int NW = BN / 64;                        // weight copies per wave per stage
-  constexpr int NA = BF16 ? 0 : NPL * (BM / 64);     // activation copies per wave per stage
+  constexpr int ST = WS_OFF + NWS * NWV * 256;
+  constexpr int NW = BN / (16 * NWV);                // weight copies per wave per stage
+  constexpr int RB = BM / (16 * NWV);                // 16-row activation blocks per wave and plane
+  constexpr int NA = BF16 ? 0 : NPL * RB;            // activation copies per wave per stage
   constexpr int XP = BF16 ? BM / 32 : 0;             // bf16 16-byte loads per thread per stage
   constexpr int ND = NW + NWS + NA;                  // copies per wave per stage
   constexpr int NV = ND + XP;                        // vector-memory instructions per stage
   static_assert(BM % 64 == 0 && BN % 64 == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
+  static_assert(BN % (16 * NWV) == 0 && BM % (16 * NWV) == 0 && (!BF16 || NWV == 4),
+                "each wave copies whole 1 KiB tiles; bf16 input uses four waves");
   static_assert(NST >= 3 && OCC * NST * ST <= 160 * 1024, "stages");
   static_assert((NST - 2) * NV < 64 && (NST - 1) * NV < 64, "wait count");
 
@@ -232,15 +238,15 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(LdsArgs a) {
   // weight-scale row: wave w copies floats (i * 4 + w) * 64 + l
   uint32_t wsoff[NWS];
 #pragma unroll
-  for (int i = 0; i < NWS; ++i) wsoff[i] = (uint32_t)min(n0 + (i * 4 + wave) * 64 + lane, a.N - 1);
+  for (int i = 0; i < NWS; ++i) wsoff[i] = (uint32_t)min(n0 + (i * NWV + wave) * 64 + lane, a.N - 1);
   // activation codes: 16-row block b = wave * (BM / 64) + i of each plane;
   // lane l copies row l / 4 of the block, chunk (l % 4) ^ ((l / 16) % 4)
   const int8_t *ab = a.xq + (int64_t)m0 * a.ld_q;
-  uint32_t aoff[BF16 ? 1 : BM / 64];
+  uint32_t aoff[BF16 ? 1 : RB];
   if (!BF16) {
 #pragma unroll
-    for (int i = 0; i < BM / 64; ++i) {
-      const int r = min(m0 + (wave * (BM / 64) + i) * 16 + (lane >> 2), a.M - 1);
+    for (int i = 0; i < RB; ++i) {
+      const int r = min(m0 + (wave * RB + i) * 16 + (lane >> 2), a.M - 1);
       const int c = (lane & 3) ^ ((lane >> 4) & 3);
       aoff[i] = (uint32_t)((r - m0) * a.ld_q + c * 16);
     }
@@ -257,14 +263,14 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(LdsArgs a) {
 #pragma unroll
     for (int i = 0; i < NWS; ++i)
       __builtin_amdgcn_global_load_lds(wsr + wsoff[i],
-                                       (lds_void *)(sb + WS_OFF + (i * 4 + wave) * 256), 4, 0, 0);
+                                       (lds_void *)(sb + WS_OFF + (i * NWV + wave) * 256), 4, 0, 0);
     if (!BF16) {
 #pragma unroll
       for (int p = 0; p < NPL; ++p) {
         const int8_t *ak = ab + p * a.plane_stride + kt * 64;
 #pragma unroll
-        for (int i = 0; i < BM / 64; ++i)
-          lds_dma16(ak + aoff[i], sb + W_ST + p * A_PL + (wave * (BM / 64) + i) * 1024);
+        for (int i = 0; i < RB; ++i)
+          lds_dma16(ak + aoff[i], sb + W_ST + p * A_PL + (wave * RB + i) * 1024);
       }
     }
   };
@@ -583,41 +589,43 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(LdsArgs a) {
 // Bytes of one stage buffer, and the stage count for a tile and input mode:
 // four when they fit in 160 KiB of LDS (bf16 input needs four), else three;
 // 0 when the configuration does not fit.
-constexpr int lds_stage_bytes(int BM, int BN, int AM) {
-  return BN * 64 + ((AM == LA_PLANES || AM == LA_BF16) ? 2 : 1) * BM * 64 + ((BN + 255) / 256) * 1024;
+constexpr int lds_stage_bytes(int BM, int BN, int AM, int NWV) {
+  return BN * 64 + ((AM == LA_PLANES || AM == LA_BF16) ? 2 : 1) * BM * 64 +
+         ((BN + 64 * NWV - 1) / (64 * NWV)) * NWV * 256;
 }
 // (occ workgroups per CU share its 160 KiB)
-constexpr int lds_stages(int BM, int BN, int AM, int occ) {
+constexpr int lds_stages(int BM, int BN, int AM, int occ, int NWV) {
   // bf16 input: exactly four (the register slots' parity); int8 input: as
   // many as fit, up to seven (copies in flight NST - 1 stages ahead)
   return (AM == LA_BF16 || AM == LA_BF16_1)
-             ? (4 * lds_stage_bytes(BM, BN, AM) <= 160 * 1024 / occ ? 4 : 0)
-             : ((160 * 1024 / occ) / lds_stage_bytes(BM, BN, AM) >= 7
+             ? (4 * lds_stage_bytes(BM, BN, AM, NWV) <= 160 * 1024 / occ ? 4 : 0)
+             : ((160 * 1024 / occ) / lds_stage_bytes(BM, BN, AM, NWV) >= 7
                     ? 7
-                    : ((160 * 1024 / occ) / lds_stage_bytes(BM, BN, AM) >= 3
-                           ? (160 * 1024 / occ) / lds_stage_bytes(BM, BN, AM)
+                    : ((160 * 1024 / occ) / lds_stage_bytes(BM, BN, AM, NWV) >= 3
+                           ? (160 * 1024 / occ) / lds_stage_bytes(BM, BN, AM, NWV)
                            : 0));
 }
 
-// One configuration per activation input, segment folds MULTI only (the
-// calls routed here have several K-segments):
-//   int8 codes  128 x 128 tiles, two workgroups per CU (256 registers per
-//               lane each): one workgroup's MFMAs run while the other waits
-//               on its copies
-//   bf16        128 x 192 tiles, one workgroup per CU (the quantisation
-//               needs the registers)
-template <int BM, int BN, int WGM, int AM, int OCC>
+// One configuration per activation input:
+//   signed codes  128 x 256 tiles of eight waves (64 x 64 each), one
+//                 workgroup per CU: two waves per SIMD, and a quarter fewer
+//                 bytes copied per product than 128 x 128
+//   two planes    128 x 128 tiles of four waves, two workgroups per CU (the
+//                 eight-wave tile spills with two activation planes)
+//   bf16          128 x 192 tiles, one workgroup per CU (the quantisation
+//                 needs the registers)
+template <int BM, int BN, int WGM, int AM, int OCC, int NWV>
 hipError_t launch_lds_mode(LdsArgs t, bool debug, hipStream_t s) {
-  constexpr int NST = lds_stages(BM, BN, AM, OCC);
+  constexpr int NST = lds_stages(BM, BN, AM, OCC, NWV);
   static_assert(NST > 0, "configuration does not fit in LDS");
   t.tiles_m = (t.M + BM - 1) / BM;
   t.tiles_n = (t.N + BN - 1) / BN;
-  dim3 grid((unsigned)(t.tiles_m * t.tiles_n)), block(256);
+  dim3 grid((unsigned)(t.tiles_m * t.tiles_n)), block(64 * NWV);
   if (debug)
-    hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, WGM, AM, NST, true, OCC>), grid, block, 0,
+    hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, WGM, AM, NST, true, OCC, NWV>), grid, block, 0,
                        s, t);
   else
-    hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, WGM, AM, NST, false, OCC>), grid, block,
+    hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, WGM, AM, NST, false, OCC, NWV>), grid, block,
                        0, s, t);
   return hipGetLastError();
 }
@@ -644,11 +652,11 @@ hipError_t launch_gemm_lds(const GemmProblem &p, hipStream_t s) {
   for (int i = 0; i < p.ks.n; ++i) t.seg_end_tile[i] = (p.ks.end[i] + 63) / 64;
   const bool debug = p.acc_debug != nullptr;
   if (p.x)
-    return p.single_scale ? launch_lds_mode<128, 192, 2, LA_BF16_1, 1>(t, debug, s)
-                          : launch_lds_mode<128, 192, 2, LA_BF16, 1>(t, debug, s);
-  if (p.single_scale) return launch_lds_mode<128, 128, 2, LA_SIGNED_1, 2>(t, debug, s);
-  return p.q_layout == 1 ? launch_lds_mode<128, 128, 2, LA_PLANES, 2>(t, debug, s)
-                         : launch_lds_mode<128, 128, 2, LA_SIGNED, 2>(t, debug, s);
+    return p.single_scale ? launch_lds_mode<128, 192, 2, LA_BF16_1, 1, 4>(t, debug, s)
+                          : launch_lds_mode<128, 192, 2, LA_BF16, 1, 4>(t, debug, s);
+  if (p.single_scale) return launch_lds_mode<128, 256, 2, LA_SIGNED_1, 1, 8>(t, debug, s);
+  return p.q_layout == 1 ? launch_lds_mode<128, 128, 2, LA_PLANES, 2, 4>(t, debug, s)
+                         : launch_lds_mode<128, 256, 2, LA_SIGNED, 1, 8>(t, debug, s);
 }
 
 }  // namespace sq
