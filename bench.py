@@ -931,6 +931,14 @@ def main():
                 gms = lay.gemm_ms(stream, 1, 10, use_graph, min_seconds=0.05)
                 summary[name]["gemm_us_per_launch"] = gms * 1e3
                 summary[name]["gemm_frac"] = lay.metrics(gms)["frac"]
+                # the pages' single launch: the same call with the quantisation
+                # fused into the GEMM (SEGQ_GEMM_FUSED_QUANT, no workspace)
+                work, flags = lay.work, lay.flags
+                lay.work, lay.flags = None, flags | S.SEGQ_GEMM_FUSED_QUANT
+                msf, _ = lay.time(stream, 1, 10, use_graph, min_seconds=0.05)
+                lay.work, lay.flags = work, flags
+                summary[name]["single_launch_us_per_step"] = msf * 1e3
+                summary[name]["single_launch_over_two"] = msf / ms
             lay.free()
             del lay
             torch.cuda.empty_cache()
