@@ -219,8 +219,10 @@ SINGLE_CASES = [
     (2, 1536, 576, [1536], "silu"),            # streaming small-M kernel, both halves in one operand
     (12, 640, 256, [64] * 10, "blocks"),       # streaming small-M kernel, ten segments
     (333, 512, 320, [512], "gelu"),            # tile kernel, one segment
-    (77, 384, 768, [128, 256], "gelu"),        # tile kernel, segments ending on whole stages
-    (130, 704, 64, [64, 128, 512], "normal"),  # tile kernel, a segment ending inside a stage
+    (77, 384, 768, [128, 256], "gelu"),        # bf16: tile kernel, segments ending on whole stages;
+                                               # codes: the LDS-staged kernel (eight-wave tiles)
+    (130, 704, 64, [64, 128, 512], "normal"),  # bf16: tile kernel, a segment ending inside a stage;
+                                               # codes: the LDS-staged kernel
     (200, 1536, 1536, [64] * 24, "blocks"),    # tile kernel, one k-step per segment; quantise-first
     (300, 512, 2304, [512], "gelu"),           # tile kernel, one segment, quantise-first
     (1641, 320, 1904, [320], "gelu"),          # tile kernel, one segment on 64 x 384 tiles
@@ -298,8 +300,9 @@ def test_halves_choice_on_nonnegative_input(M, K, N, kseg, mode):
 @pytest.mark.parametrize("nk", [1, 4])
 def test_gemm_at_the_int32_bound(M, mode, nk):
     """K = 132096 (the largest multiple of 64 within SEGQ_MAX_KSEG_WIDTH) in
-    one K-segment, or four (the tile kernel's int32 running sums then span
-    all of K), with operands that put every accumulator at its largest
+    one K-segment, or four (on bf16 input the tile kernel's int32 running
+    sums then span all of K; on codes the LDS-staged kernel folds each
+    segment's own sums), with operands that put every accumulator at its largest
     magnitude: rows of -1 quantise to -128 throughout, rows of +1 to 127,
     columns of -0.02 / +0.02 to -127 / 127, so one segment's A- reaches
     132096 * 128 * 127 = 2147352576 (2^31 - 131072).  The chunked small-M
