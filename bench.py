@@ -446,6 +446,8 @@ def measured_peaks(dev, stream, slab_bytes: int = 0, sustain_s: float = 1.0):
     lib.sqprobe_mfma_i8.argtypes = [I64, I32, I32, P, P, P]
     lib.sqprobe_stream_read.argtypes = [P, I64, I32, P, P]
     lib.sqprobe_ops_per_mfma.restype = I64
+    lib.sqprobe_mfma_i8_data.argtypes = [I64, I32, I32, P, P, P, P]
+    lib.sqprobe_mfma_data_bytes_per_wave.restype = I64
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     sp = ctypes.c_void_p(stream.cuda_stream)
     khz = lib.sqprobe_wall_clock_khz()
@@ -521,6 +523,34 @@ def measured_peaks(dev, stream, slab_bytes: int = 0, sustain_s: float = 1.0):
         out["mfma_loop_sustained_tops"] = ops / t / 1e12
         out["shader_clock_ghz_sustained_mfma"] = ratio * khz * 1e3 / 1e9 if khz > 0 else None
         out["mfma_loop_sustained_seconds"] = n * t
+        # the same, sustained, on random operands that change every instruction
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0)
+        src = torch.randint(-128, 128, (waves * lib.sqprobe_mfma_data_bytes_per_wave(),),
+                            dtype=torch.int8, device=dev, generator=gen)
+
+        def run_data():
+            rc = lib.sqprobe_mfma_i8_data(iters, blocks, 4, ctypes.c_void_p(src.data_ptr()),
+                                          ctypes.c_void_p(sink.data_ptr()),
+                                          ctypes.c_void_p(spans.data_ptr()), sp)
+            if rc != 0:
+                raise RuntimeError(f"sqprobe_mfma_i8_data failed ({rc})")
+        with torch.cuda.stream(stream):
+            t1 = timed(run_data, 1)
+            n = max(32, int(sustain_s / t1))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for i in range(n):
+                if i == n - last:
+                    e0.record(stream)
+                run_data()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / last
+        sv = spans.view(-1, 2).cpu().double()
+        ratio = float((sv[:, 0] / sv[:, 1].clamp(min=1)).median())
+        out["mfma_loop_data_tops"] = ops / t / 1e12
+        out["shader_clock_ghz_data_mfma"] = ratio * khz * 1e3 / 1e9 if khz > 0 else None
+        del src
     nbytes = 1 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.fill_(1)
@@ -573,7 +603,8 @@ def measured_peaks(dev, stream, slab_bytes: int = 0, sustain_s: float = 1.0):
                      f"independent accumulators per wave, 4 waves per workgroup, 1 and 2 "
                      f"workgroups per CU ({cus} CUs), clock = shader/constant clock ratio "
                      f"over the loop; the 1-per-CU loop again back to back for about "
-                     f"{sustain_s:g} s, rate and clock over the last launches (sustained); "
+                     f"{sustain_s:g} s, rate and clock over the last launches (sustained), and "
+                     f"likewise on random operands that change every instruction (data); "
                      f"grid-stride 16-byte read of 1 GiB; torch copy of 512 MiB; "
                      f"best of 3-5 timed launches; slab: grid-stride reads of slab_bytes from "
                      f"{nbytes // max(slab_bytes, 1) if slab_bytes else 0} distinct slices, one launch "
@@ -975,8 +1006,11 @@ def main():
             roof["stream_floor_us"] = mp["hbm_stream_slab_us"]
             roof["over_stream_floor"] = roof["per_launch"]["avg_us"] / mp["hbm_stream_slab_us"]
         sus = mp.get("mfma_loop_sustained_tops")
+        dat = mp.get("mfma_loop_data_tops")
         if roof["bound"] != "hbm" and sus:
             roof["frac_of_sustained_mfma"] = roof["achieved"] / sus
+        if roof["bound"] != "hbm" and dat:
+            roof["frac_of_data_mfma"] = roof["achieved"] / dat
         for v in line.get("all_workloads", {}).values():
             ref = mp["hbm_read_gbs"] if v["bound"] == "hbm" else mp["int8_mfma_tops"]
             v["frac_of_measured"] = v["value"] / ref
@@ -984,6 +1018,10 @@ def main():
                 v["frac_of_sustained_mfma"] = v["value"] / sus
                 if v.get("gemm_us_per_launch"):
                     v["gemm_frac_of_sustained_mfma"] = v["gemm_frac"] * PEAK_INT8_TOPS / sus
+            if v["bound"] != "hbm" and dat:
+                v["frac_of_data_mfma"] = v["value"] / dat
+                if v.get("gemm_us_per_launch"):
+                    v["gemm_frac_of_data_mfma"] = v["gemm_frac"] * PEAK_INT8_TOPS / dat
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, x_host, w_host)
     print(json.dumps(line), flush=True)

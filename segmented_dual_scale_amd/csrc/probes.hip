@@ -48,6 +48,54 @@ __global__ __launch_bounds__(256) void mfma_i8_kernel(int64_t iters, int32_t *si
   }
 }
 
+// The same loop on operands that change from one instruction to the next:
+// each lane loads eight A and eight B fragments of random bytes (256 bytes,
+// at src + (wave * 64 + lane) * 256) and every instruction of an iteration
+// pairs a different A with a different B, the pairing shifting between
+// even and odd iterations.  Constant operands leave the matrix core's data
+// path idle; the layer's operands do not, and the power they draw sets the
+// clock the layer gets.
+constexpr int kDataFrags = 8;
+__global__ __launch_bounds__(256) void mfma_i8_data_kernel(int64_t iters, const v4i *src,
+                                                           int32_t *sink, uint64_t *spans) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const v4i *mine = src + (gw * 64 + lane) * (2 * kDataFrags);
+  v4i a[kDataFrags], b[kDataFrags];
+#pragma unroll
+  for (int f = 0; f < kDataFrags; ++f) {
+    a[f] = mine[f];
+    b[f] = mine[kDataFrags + f];
+  }
+  v16i acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = v16i{};
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t w0 = __builtin_amdgcn_s_memrealtime();
+  for (int64_t i = 0; i < iters; i += 2) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c % kDataFrags], b[(c + 3) % kDataFrags],
+                                                     acc[c], 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[(c + 5) % kDataFrags],
+                                                     b[(c + 1) % kDataFrags], acc[c], 0, 0, 0);
+  }
+  int32_t s = 0;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s ^= acc[c][r];
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  const uint64_t w1 = __builtin_amdgcn_s_memrealtime();
+  sink[gw * 64 + lane] = s;
+  if (lane == 0) {
+    spans[2 * gw] = c1 - c0;
+    spans[2 * gw + 1] = w1 - w0;
+  }
+}
+
 // Grid-stride read of n16 16-byte vectors; one XOR checksum per thread.
 __global__ __launch_bounds__(256) void stream_read_kernel(const v4u *src, int64_t n16,
                                                           uint32_t *sink) {
@@ -81,6 +129,22 @@ int sqprobe_mfma_i8(int64_t iters, int32_t blocks, int32_t waves_per_block, int3
                      (hipStream_t)stream, iters, sink, spans);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
+
+// The matrix-core probe on changing operands (see mfma_i8_data_kernel):
+// `iters` even; src: device bytes [blocks * waves_per_block * 64 * 256],
+// 16-byte aligned, random; sink and spans as for sqprobe_mfma_i8.
+int sqprobe_mfma_i8_data(int64_t iters, int32_t blocks, int32_t waves_per_block, const void *src,
+                         int32_t *sink, uint64_t *spans, void *stream) {
+  if (iters < 2 || iters % 2 || blocks < 1 || waves_per_block < 1 || waves_per_block > 4 ||
+      !src || (reinterpret_cast<uintptr_t>(src) & 15u) || !sink || !spans)
+    return -1;
+  hipLaunchKernelGGL(mfma_i8_data_kernel, dim3((unsigned)blocks), dim3(64u * waves_per_block), 0,
+                     (hipStream_t)stream, iters, static_cast<const v4i *>(src), sink, spans);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Bytes of random operand data sqprobe_mfma_i8_data reads per wave.
+int64_t sqprobe_mfma_data_bytes_per_wave(void) { return 64LL * 2 * kDataFrags * 16; }
 
 // Streaming-read probe over `bytes` (a multiple of 16, 16-byte aligned src).
 // sink: device uint32 [blocks * 256].
