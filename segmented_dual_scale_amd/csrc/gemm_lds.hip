@@ -49,13 +49,12 @@
 //     are: y += c+ A+ + c- A-.  Single-scale: one product on the signed code.
 //     (c+-_i = s+-_i * w_scale[i][n].)
 //   * int8 input: 64 x 64 per wave, two waves per SIMD (256 registers per
-//     lane each): signed codes on 128 x 256 tiles of eight waves, one
-//     workgroup per CU; two planes on 128 x 128 tiles of four, two per CU.
+//     lane each): 128 x 128 tiles of four waves, two workgroups per CU.  The
+//     kernel also takes eight-wave workgroups (NWV = 8).
 //     Measured on MI355X, the copies' issue and the bytes moved bound this
 //     kernel more than the matrix cores: without the copies it runs about
 //     a fifth faster, and the shader clock under it falls well below the
-//     clock of a matrix-core-only loop.  The wider tile copies a quarter
-//     fewer bytes per product.
+//     clock of a matrix-core-only loop.
 //   * Tile order is XCD-aware: workgroups are dealt to the 8 XCDs in turn, so
 //     XCD x receives one contiguous range of logical tiles, ordered in
 //     groups of 8 row tiles so that the tiles one XCD runs at once share
@@ -607,13 +606,13 @@ constexpr int lds_stages(int BM, int BN, int AM, int occ, int NWV) {
 }
 
 // One configuration per activation input:
-//   signed codes  128 x 256 tiles of eight waves (64 x 64 each), one
-//                 workgroup per CU: two waves per SIMD, and a quarter fewer
-//                 bytes copied per product than 128 x 128
-//   two planes    128 x 128 tiles of four waves, two workgroups per CU (the
-//                 eight-wave tile spills with two activation planes)
-//   bf16          128 x 192 tiles, one workgroup per CU (the quantisation
-//                 needs the registers)
+//   int8 codes  128 x 128 tiles of four waves (64 x 64 each), two
+//               workgroups per CU.  (128 x 256 tiles of eight waves, one
+//               workgroup per CU, copy a quarter fewer bytes per product;
+//               measured on four MI355X boxes they were 2.5-4 % faster on
+//               two and 7-13 % slower on the other two.)
+//   bf16        128 x 192 tiles, one workgroup per CU (the quantisation
+//               needs the registers)
 template <int BM, int BN, int WGM, int AM, int OCC, int NWV>
 hipError_t launch_lds_mode(LdsArgs t, bool debug, hipStream_t s) {
   constexpr int NST = lds_stages(BM, BN, AM, OCC, NWV);
@@ -654,9 +653,9 @@ hipError_t launch_gemm_lds(const GemmProblem &p, hipStream_t s) {
   if (p.x)
     return p.single_scale ? launch_lds_mode<128, 192, 2, LA_BF16_1, 1, 4>(t, debug, s)
                           : launch_lds_mode<128, 192, 2, LA_BF16, 1, 4>(t, debug, s);
-  if (p.single_scale) return launch_lds_mode<128, 256, 2, LA_SIGNED_1, 1, 8>(t, debug, s);
+  if (p.single_scale) return launch_lds_mode<128, 128, 2, LA_SIGNED_1, 2, 4>(t, debug, s);
   return p.q_layout == 1 ? launch_lds_mode<128, 128, 2, LA_PLANES, 2, 4>(t, debug, s)
-                         : launch_lds_mode<128, 256, 2, LA_SIGNED, 1, 8>(t, debug, s);
+                         : launch_lds_mode<128, 128, 2, LA_SIGNED, 2, 4>(t, debug, s);
 }
 
 }  // namespace sq
