@@ -369,8 +369,14 @@ size_t segquant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t n_
  */
 int segquant_gemm_halves(const float *act_scales_host, int32_t n_kseg);
 
-/* Which kernel segquant_gemm_w8a8_seg runs for this shape under `flags`
- * (SEGQ_KERNEL_*), or a negative status when the shape is invalid. */
+/* Which kernel family segquant_gemm_w8a8_seg runs for this shape under
+ * `flags` (SEGQ_KERNEL_*), or a negative status when the shape is invalid.
+ * SEGQ_KERNEL_TILE is the large-M family: the tile kernel, or, for several
+ * K-segments on int8 codes (the quantise-first path included) and for any
+ * call whose K exceeds the tile kernel's running int32 sums
+ * (K * 128 * 127 >= 2^31), the kernel that stages both operands in LDS and
+ * folds each segment's own sums; which of the two depends on the segment
+ * list and the activation format, not on the shape alone. */
 int segquant_gemm_kernel_for(int64_t M, int64_t N, int64_t K, uint32_t flags);
 
 /* Text for a status code (static storage). */

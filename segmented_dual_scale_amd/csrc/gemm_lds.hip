@@ -18,9 +18,10 @@
 // products ever sit in an int32 accumulator.
 //
 // Design (CDNA4):
-//   * A workgroup of 4 waves owns a BM x BN output tile; the waves form a
-//     WGM x (4 / WGM) grid, each owning a WM x WN sub-tile of 32 x 32 blocks
-//     computed by the int8 32x32x32 matrix-core instruction.
+//   * A workgroup of NWV waves (4, or 8 for int8 input) owns a BM x BN
+//     output tile; the waves form a WGM x (NWV / WGM) grid, each owning a
+//     WM x WN sub-tile of 32 x 32 blocks computed by the int8 32x32x32
+//     matrix-core instruction.
 //   * K advances in stages of 64 (one packed weight k-tile; K-segment
 //     boundaries are multiples of 64, so every stage lies in one segment).
 //     NST stage buffers rotate in LDS.  Each holds the stage's weight tiles,
@@ -49,12 +50,12 @@
 //     are: y += c+ A+ + c- A-.  Single-scale: one product on the signed code.
 //     (c+-_i = s+-_i * w_scale[i][n].)
 //   * int8 input: 64 x 64 per wave, two waves per SIMD (256 registers per
-//     lane each): 128 x 128 tiles of four waves, two workgroups per CU.  The
-//     kernel also takes eight-wave workgroups (NWV = 8).
-//     Measured on MI355X, the copies' issue and the bytes moved bound this
-//     kernel more than the matrix cores: without the copies it runs about
-//     a fifth faster, and the shader clock under it falls well below the
-//     clock of a matrix-core-only loop.
+//     lane each): 128 x 128 tiles of four waves, two workgroups per CU.
+//     Measured on MI355X, the copies' issue costs about a sixth of the time
+//     (the kernel runs that much faster with them removed), and the shader
+//     clock under it (about 1.8 GHz) is set by the power the matrix cores
+//     draw on changing operands, as for a matrix-core-only loop on random
+//     data.
 //   * Tile order is XCD-aware: workgroups are dealt to the 8 XCDs in turn, so
 //     XCD x receives one contiguous range of logical tiles, ordered in
 //     groups of 8 row tiles so that the tiles one XCD runs at once share
